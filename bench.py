@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X MoE-layer hot path: one step = route -> dispatch -> expert MLP -> combine
+over one batch of synthetic tokens, inputs resident in HBM, on one GPU.
+
+Prints ONE JSON line: MoE-layer tokens/s (whole step), per-stage times, dispatch+combine GB/s against
+the HBM peak, the roofline of the dominant stage (the expert-MLP grouped GEMM) and the CPU oracle timed
+on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps 32] [--warmup 16] [--workload mixtral8x7b-decode]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s on 1 MI355X; dispatch+combine GB/s and % HBM peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MFMA_F32_PEAK_TFLOPS = 157.3
+DEFAULT_WORKLOAD = 2            # Mixtral-8x7B-shaped decode layer
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default=None,
+                    help="workload name or number (default: mixtral8x7b-decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    return ap.parse_args()
+
+
+def pick_workload(name):
+    import moe_workloads as W
+    if name is None:
+        return W.CONFIGS[DEFAULT_WORKLOAD]
+    for c in W.CONFIGS.values():
+        if name == c.name or name == str(c.idx):
+            return c
+    raise SystemExit(f"unknown workload {name!r}; choose from {[c.name for c in W.CONFIGS.values()]}")
+
+
+def algorithmic_bytes(cfg, C, counts, s):
+    """Bytes each stage must move (what the method needs, not what the kernels happen to move)."""
+    T, H, E, k, F, El = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.El
+    kept = counts["kept"]
+    touched = counts["tokens_touched"]
+    active_local = counts["active_local"]
+    bias = 0 if counts["bias_stride"] is None else (E * 4 if counts["bias_stride"] == 0 else T * E * 4)
+    route = T * H * s + E * H * 4 + bias + T * E * 4 + T * k * 8
+    dispatch = touched * H * s + kept * H * s + kept * 8 + 2 * T * k * 4 + E * 16
+    combine = kept * H * s + T * k * 8 + T * H * s
+    mlp = active_local * 3 * H * F * s + 2 * kept * H * s
+    return dict(route=route, dispatch=dispatch, combine=combine, mlp=mlp,
+                route_flops=2 * T * E * H, mlp_flops=6 * H * F * kept)
+
+
+def cpu_baseline(cfg, inp_dev, max_tokens=None):
+    """Time the CPU oracle (as it stands) on the first tokens of the same workload."""
+    import numpy as np
+    import torch
+
+    import moe_workloads as W
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - report the affinity if the BLAS pool cannot be queried
+        threads = len(os.sched_getaffinity(0))
+
+    def host(t):
+        if t is None:
+            return None
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    T = cfg.T if max_tokens is None else min(cfg.T, max_tokens)
+    dt = cfg.dtype
+    x = host(inp_dev["x"][:T])
+    bias = inp_dev["bias"]
+    bias = None if bias is None else host(bias if bias.dim() == 1 else bias[:T])
+    wr = host(inp_dev["w_router"])
+    wgu = host(inp_dev["w_gate_up"])
+    wdn = host(inp_dev["w_down"])
+    C = W.capacity(cfg, T)
+    t0 = time.perf_counter()
+    res = oracle.moe_layer(x, dt, wr, bias, cfg.k, C, cfg.R, wgu, wdn, cfg.F)
+    sec = time.perf_counter() - t0
+    sample = (f"the whole {cfg.name} batch ({T} tokens, one oracle run)" if T == cfg.T else
+              f"the first {T} of {cfg.T} tokens of {cfg.name} as one batch (capacity {C}), one oracle run")
+    return dict(value=T / sec, unit="tokens/s", cores=int(threads), kind="oracle", sample=sample,
+                seconds=round(sec, 3), rows=int(res["layout"].total))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no collectives or "
+              f"multi-GPU path; the single-GPU figure is the per-GPU share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import combine_router_gemm_amd as moe
+    import moe_workloads as W
+
+    cfg = pick_workload(args.workload)
+    torch.cuda.set_device(0)
+    moe.load_library()
+    dev = torch.device("cuda:0")
+    print(f"[bench] {W.describe(cfg)} steps={args.steps} warmup={args.warmup}", file=sys.stderr, flush=True)
+    inp = W.make_inputs(cfg, device=dev)
+    T, H, E, k, R, F = cfg.T, cfg.H, cfg.E, cfg.k, cfg.R, cfg.F
+    C = inp["C"]
+    x = inp["x"]
+    s = x.element_size()
+
+    # every buffer and workspace is allocated once, outside the timed region
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+    L = moe.Layout(T, k, E, R, C, H, device=dev)
+    send_buf = torch.empty(L.rows_max, H, dtype=x.dtype, device=dev)
+    out_buf = torch.empty_like(send_buf)
+    y = torch.empty(T, H, dtype=x.dtype, device=dev)
+    xdt = moe.MOE_BF16 if x.dtype == torch.bfloat16 else moe.MOE_F32
+    ws_route = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E)), dtype=torch.uint8, device=dev)
+    ws_disp = torch.empty(max(1, moe.moe_dispatch_workspace_bytes(T, k, E)), dtype=torch.uint8, device=dev)
+    ws_mlp = torch.empty(max(1, moe.moe_expert_mlp_workspace_bytes(T, k, E, R, C, F, xdt)), dtype=torch.uint8,
+                         device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_route(x, inp["w_router"], inp["bias"], k, logits, ids, wts, workspace=ws_route)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.moe_dispatch(x, ids, L, send_buf, workspace=ws_disp)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.moe_expert_mlp(send_buf, L, inp["w_gate_up"], inp["w_down"], out_buf, workspace=ws_mlp)
+        if ev is not None:
+            ev[3].record(stream)
+        moe.moe_combine(out_buf, L, wts, y)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, bracketed by device synchronisation
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage = {"route": 0.0, "dispatch": 0.0, "expert_mlp": 0.0, "combine": 0.0}
+    names = list(stage)
+    for ev in events:
+        for j, n in enumerate(names):
+            stage[n] += ev[j].elapsed_time(ev[j + 1])
+    stage_us = {n: 1e3 * v / args.steps for n, v in stage.items()}
+    gpu_step_us = sum(stage_us.values())
+    ms_per_step = 1e3 * wall / args.steps
+
+    # routing outcome of the (deterministic) step, read back after the timed region
+    kept = int(L.expert_kept.sum().item())
+    kept_per_e = L.expert_kept.cpu()
+    active_local = int((kept_per_e.view(R, cfg.El).sum(0) > 0).sum().item())
+    pr = L.pair_row.cpu()
+    touched = int((pr >= 0).any(dim=1).sum().item())
+    counts = dict(kept=kept, tokens_touched=touched, active_local=active_local,
+                  bias_stride=None if inp["bias"] is None else inp["bias_stride"])
+    ab = algorithmic_bytes(cfg, C, counts, s)
+
+    mlp_s = stage_us["expert_mlp"] * 1e-6
+    mlp_ai = ab["mlp_flops"] / max(ab["mlp"], 1)
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if s == 2 else MFMA_F32_PEAK_TFLOPS
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mlp_ai >= ridge:
+        achieved = ab["mlp_flops"] / mlp_s / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=mfma_peak, unit="TFLOP/s",
+                    frac=round(achieved / mfma_peak, 4), traffic=None)
+    else:
+        achieved = ab["mlp"] / mlp_s / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+    roof["kernel"] = "moe_expert_mlp (grouped GEMM: plan + gate/up + down launches)"
+    roof["algorithmic_bytes"] = ab["mlp"]
+    roof["algorithmic_flops"] = ab["mlp_flops"]
+
+    dc_s = (stage_us["dispatch"] + stage_us["combine"]) * 1e-6
+    dc_gbs = (ab["dispatch"] + ab["combine"]) / dc_s / 1e9
+    tokens_per_s = T / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s == 2 else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "ffn": F,
+                   "dest_ranks": R, "capacity": C, "routing": cfg.routing, "act_dtype": cfg.dtype},
+        "roofline": roof,
+        "stages_us": {n: round(v, 2) for n, v in stage_us.items()},
+        "gpu_step_us_events": round(gpu_step_us, 2),
+        "dispatch_combine": {"GB/s": round(dc_gbs, 1), "frac_hbm_peak": round(dc_gbs / HBM_PEAK_GBS, 4),
+                             "bytes": ab["dispatch"] + ab["combine"]},
+        "route": {"TFLOP/s": round(ab["route_flops"] / (stage_us["route"] * 1e-6) / 1e12, 3),
+                  "GB/s": round(ab["route"] / (stage_us["route"] * 1e-6) / 1e9, 1)},
+        "effective_assignments_per_s": round(kept / (ms_per_step * 1e-3), 1),
+        "routing": {"kept_pairs": kept, "pairs": T * k, "dropped_pairs": T * k - kept,
+                    "active_local_experts": active_local},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        sample_tokens = None if cfg.T <= 512 else 256
+        print(f"[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, sample_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+// C ABI of the MoE-layer hot path: argument validation on the host, workspace carving, launches.
+// Every entry point validates before its first HIP call, allocates nothing and only enqueues work on
+// the caller's stream.
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+// Compute units of the current device (cached per device id; a benign race fills the same value).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+// the split-K plan of the router is fixed for the target chip (256 CUs), so the workspace size is a
+// function of the shape alone
+constexpr int ROUTE_PLAN_CUS = 256;
+
+bool valid_dtype(moe_dtype_t d) { return d == MOE_F32 || d == MOE_BF16; }
+
+int check_layout(const moe_layout_t* L) {
+  if (!L) return MOE_ERR_INVALID;
+  if (L->T < 0 || L->C < 0 || L->E < 1 || L->R < 1 || L->k < 1 || L->H < 1) return MOE_ERR_INVALID;
+  if (L->E > MOE_MAX_EXPERTS || L->k > MOE_MAX_TOPK || L->k > L->E) return MOE_ERR_INVALID;
+  if (L->E % L->R != 0) return MOE_ERR_INVALID;
+  if (L->H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)L->T * L->k > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!L->expert_count || !L->expert_kept || !L->expert_overflow || !L->expert_offset) return MOE_ERR_INVALID;
+  const int64_t rows = moe_rows_max(L->T, L->k, L->E, L->C);
+  if (rows > 0 && (!L->row_token || !L->row_slot)) return MOE_ERR_INVALID;
+  if (L->T > 0 && !L->pair_row) return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int64_t moe_rows_max(int T, int k, int E, int C) {
+  if (T <= 0 || k <= 0 || E <= 0 || C <= 0) return 0;
+  const int64_t a = (int64_t)T * k, b = (int64_t)E * C;
+  return a < b ? a : b;
+}
+
+size_t moe_route_workspace_bytes(int T, int H, int E) {
+  if (T <= 0 || H <= 0 || E <= 0) return 0;
+  const int splits = moe::route_splits(T, H, E, ROUTE_PLAN_CUS);
+  const int nsplit = moe::ceil_div_host(H, moe::route_k_split(H, splits));
+  if (nsplit <= 1) return 0;
+  return (size_t)nsplit * (size_t)T * (size_t)E * sizeof(float);
+}
+
+int moe_route(const void* x, moe_dtype_t xdt, const float* w_router, const float* logit_bias,
+              int64_t bias_row_stride, int T, int H, int E, int k, float* logits, int32_t* topk_ids,
+              float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(xdt)) return MOE_ERR_UNSUPPORTED;
+  if (T < 0 || H < 1 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK || k > E)
+    return MOE_ERR_INVALID;
+  if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (logit_bias && bias_row_stride < 0) return MOE_ERR_INVALID;
+  if ((int64_t)T * E > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits || !topk_ids || !topk_w) return MOE_ERR_INVALID;
+  const size_t need = moe_route_workspace_bytes(T, H, E);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_INVALID;
+  const int splits = moe::route_splits(T, H, E, ROUTE_PLAN_CUS);
+  float* partial = need > 0 ? static_cast<float*>(workspace) : logits;
+  return hip_status(moe::launch_route(x, xdt == MOE_BF16, w_router, logit_bias, logit_bias ? bias_row_stride : 0,
+                                      T, H, E, k, logits, topk_ids, topk_w, partial, splits, stream));
+}
+
+size_t moe_dispatch_workspace_bytes(int T, int k, int E) {
+  if (T < 0 || k < 0 || E < 0) return 0;
+  const size_t nblk = (size_t)moe::dispatch_num_blocks(T);
+  return moe::align256(nblk * (size_t)E * sizeof(int)) + moe::align256((size_t)T * k * sizeof(int));
+}
+
+int moe_dispatch(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const moe_layout_t* layout,
+                 void* send_buf, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(xdt)) return MOE_ERR_UNSUPPORTED;
+  const int st = check_layout(layout);
+  if (st != MOE_OK) return st;
+  const moe_layout_t& L = *layout;
+  const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
+  if (L.T > 0 && (!x || !topk_ids)) return MOE_ERR_INVALID;
+  if (rows > 0 && !send_buf) return MOE_ERR_INVALID;
+  const size_t need = moe_dispatch_workspace_bytes(L.T, L.k, L.E);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_INVALID;
+  char* ws = static_cast<char*>(workspace);
+  int* blk_count = reinterpret_cast<int*>(ws);
+  int* pair_local =
+      reinterpret_cast<int*>(ws + moe::align256((size_t)moe::dispatch_num_blocks(L.T) * L.E * sizeof(int)));
+  return hip_status(moe::launch_dispatch(x, xdt == MOE_BF16, topk_ids, L, send_buf, blk_count, pair_local, stream));
+}
+
+size_t moe_expert_mlp_workspace_bytes(int T, int k, int E, int R, int C, int F, moe_dtype_t xdt) {
+  if (E <= 0 || R <= 0 || E % R != 0 || F <= 0) return 0;
+  const int El = E / R;
+  const int64_t rows = moe_rows_max(T, k, E, C);
+  const size_t esz = xdt == MOE_BF16 ? 2 : 4;
+  return moe::align256(moe::mlp_plan_ints(El) * sizeof(int)) + moe::align256((size_t)rows * sizeof(int)) +
+         moe::align256((size_t)rows * (size_t)F * esz);
+}
+
+int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* layout, const void* w_gate_up,
+                   const void* w_down, int F, void* out_buf, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  if (!valid_dtype(xdt)) return MOE_ERR_UNSUPPORTED;
+  const int st = check_layout(layout);
+  if (st != MOE_OK) return st;
+  const moe_layout_t& L = *layout;
+  if (F < 1) return MOE_ERR_INVALID;
+  if (F % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)2 * F > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
+  if (!w_gate_up || !w_down) return MOE_ERR_INVALID;
+  if (rows > 0 && (!send_buf || !out_buf)) return MOE_ERR_INVALID;
+  const size_t need = moe_expert_mlp_workspace_bytes(L.T, L.k, L.E, L.R, L.C, F, xdt);
+  if (!workspace || workspace_bytes < need) return MOE_ERR_INVALID;
+  const int El = L.E / L.R;
+  char* ws = static_cast<char*>(workspace);
+  int* plan = reinterpret_cast<int*>(ws);
+  ws += moe::align256(moe::mlp_plan_ints(El) * sizeof(int));
+  int* perm = reinterpret_cast<int*>(ws);
+  ws += moe::align256((size_t)rows * sizeof(int));
+  void* hbuf = ws;
+  const moe::MlpTiles tiles = moe::mlp_pick_tiles(rows, El, xdt == MOE_BF16);
+  return hip_status(moe::launch_expert_mlp(send_buf, xdt == MOE_BF16, L, w_gate_up, w_down, F, out_buf, plan, perm,
+                                           hbuf, tiles, device_cus(), stream));
+}
+
+int moe_combine(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout, const float* topk_w, void* y,
+                hipStream_t stream) {
+  if (!valid_dtype(xdt)) return MOE_ERR_UNSUPPORTED;
+  const int st = check_layout(layout);
+  if (st != MOE_OK) return st;
+  const moe_layout_t& L = *layout;
+  if (L.T == 0) return MOE_OK;
+  const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
+  if (!topk_w || !y) return MOE_ERR_INVALID;
+  if (rows > 0 && !out_buf) return MOE_ERR_INVALID;
+  return hip_status(moe::launch_combine(out_buf, xdt == MOE_BF16, L, topk_w, y, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+// Dispatch: partition (token, slot) pairs by expert into contiguous, rank-aligned per-expert rows.
+//
+// The pages' send side counts tokens per expert with on-chip atomics, turns the counts into offsets with
+// a cumulative sum and packs every token into its expert's contiguous region ("Enabling
+// trillion-parameter models on AWS EFA", section "Диспетчеризация и комбинирование"); the per-expert
+// capacity drops pairs beyond C, overflow = max(assigned - C, 0) ("80. MoE Expert Parallel
+// Benchmark", Step 2). The pages' receive side orders tokens through an atomic counter, so its order
+// is not deterministic ("Efficient and portable mixture-of-experts communication", section
+// "Dispatch"); here every row position is the stable one: pair (t, j) of expert e lands at
+// position #(earlier pairs in row-major order with expert e).
+//
+// Three kernels:
+//   dispatch_rank    one workgroup per DISPATCH_TB tokens. Each wave walks a contiguous slice of the
+//                    block's pairs 64 at a time; lanes with the same expert find each other with one
+//                    ballot per id bit (a wave-wide match), which gives the stable rank inside the 64;
+//                    one lane per distinct expert does an LDS atomic add of the group size on a
+//                    wave-private counter (per-wave counters keep the order stable). The four waves'
+//                    counts are then scanned in LDS, giving the block histogram (to blk_count) and each
+//                    pair's rank inside its block (to pair_local).
+//   dispatch_scan    one workgroup: per expert, an exclusive scan of blk_count over blocks (in place),
+//                    count / kept / overflow, then an exclusive scan of kept over experts -> offsets.
+//   dispatch_scatter one wave per token: position = block base + rank in block; kept pairs write the
+//                    layout entries, and the token row is read once and stored to each kept row with
+//                    16-byte vector loads and non-temporal stores.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int DR_THREADS = 256;
+constexpr int DR_WAVES = DR_THREADS / MOE_WAVE;
+
+__global__ __launch_bounds__(DR_THREADS) void dispatch_rank_kernel(const int* __restrict__ ids, int T, int k,
+                                                                  int E, int* __restrict__ blk_count,
+                                                                  int* __restrict__ pair_local) {
+  __shared__ int cnt[DR_WAVES][MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int i = tid; i < DR_WAVES * E; i += DR_THREADS) cnt[i / E][i % E] = 0;
+  __syncthreads();
+
+  const int64_t p_begin = (int64_t)blockIdx.x * DISPATCH_TB * k;
+  const int64_t p_end = min((int64_t)(blockIdx.x + 1) * DISPATCH_TB, (int64_t)T) * k;
+  // each wave takes DISPATCH_TB * k / DR_WAVES = 64 * k consecutive pairs: k chunks of 64
+  const int64_t w_begin = p_begin + (int64_t)wave * 64 * k;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+
+  int myrank[MOE_MAX_TOPK];
+  int mye[MOE_MAX_TOPK];
+#pragma unroll
+  for (int c = 0; c < MOE_MAX_TOPK; ++c) {
+    myrank[c] = 0;
+    mye[c] = -1;
+    if (c < k) {
+      const int64_t p = w_begin + (int64_t)c * 64 + lane;
+      int e = -1;
+      if (p < p_end) {
+        e = ids[p];
+        if (e < 0 || e >= E) e = -1;  // out-of-range ids are ignored
+      }
+      const bool valid = e >= 0;
+      uint64_t same = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
+      }
+      // one LDS atomic per distinct expert in the 64 pairs: the highest lane of each group of equal
+      // ids adds the group size to the wave's counter and hands the old value to its group
+      const int leader = valid ? 63 - __clzll(same) : lane;
+      int old = 0;
+      if (valid && lane == leader) old = atomicAdd(&cnt[wave][e], __popcll(same));
+      const int base = __shfl(old, leader, 64);
+      if (valid) {
+        myrank[c] = base + __popcll(same & lanemask_lt());
+        mye[c] = e;
+      }
+    }
+  }
+  __syncthreads();
+  // exclusive scan over the waves (pair order), per expert; the block total is the histogram row
+  for (int e = tid; e < E; e += DR_THREADS) {
+    int acc = 0;
+#pragma unroll
+    for (int w = 0; w < DR_WAVES; ++w) {
+      const int c = cnt[w][e];
+      cnt[w][e] = acc;
+      acc += c;
+    }
+    blk_count[(int64_t)blockIdx.x * E + e] = acc;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < MOE_MAX_TOPK; ++c) {
+    if (c < k) {
+      const int64_t p = w_begin + (int64_t)c * 64 + lane;
+      if (p < p_end) pair_local[p] = mye[c] >= 0 ? cnt[wave][mye[c]] + myrank[c] : -1;
+    }
+  }
+}
+
+constexpr int DS_THREADS = 512;  // >= MOE_MAX_EXPERTS: one thread per expert
+
+__global__ __launch_bounds__(DS_THREADS) void dispatch_scan_kernel(int* __restrict__ blk_count, int nblk, int E,
+                                                                  int C, int* __restrict__ count,
+                                                                  int* __restrict__ kept,
+                                                                  int* __restrict__ overflow,
+                                                                  int* __restrict__ offset) {
+  __shared__ int wsum[DS_THREADS / MOE_WAVE];
+  const int e = threadIdx.x;
+  const int lane = e & 63;
+  const int wave = e >> 6;
+  int total = 0;
+  if (e < E) {
+    for (int b = 0; b < nblk; ++b) {
+      const int c = blk_count[(int64_t)b * E + e];
+      blk_count[(int64_t)b * E + e] = total;  // becomes the block's base position for expert e
+      total += c;
+    }
+  }
+  const int kp = e < E ? min(total, C) : 0;
+  if (e < E) {
+    count[e] = total;
+    kept[e] = kp;
+    overflow[e] = total - kp;
+  }
+  // exclusive scan of kept over experts: wave-level inclusive scan, then wave totals
+  int incl = kp;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += wsum[w];
+  if (e < E) offset[e] = wbase + incl - kp;
+  if (e == E - 1) offset[E] = wbase + incl;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const T* __restrict__ x, const int* __restrict__ ids,
+                                                              int T_, int H, int k, int E, int C,
+                                                              const int* __restrict__ blk_base,
+                                                              const int* __restrict__ pair_local,
+                                                              const int* __restrict__ offset,
+                                                              int* __restrict__ row_token, int* __restrict__ row_slot,
+                                                              int* __restrict__ pair_row, T* __restrict__ send_buf) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  int row = -1;
+  if (lane < k) {
+    const int64_t p = (int64_t)t * k + lane;
+    const int e = ids[p];
+    const int local = pair_local[p];
+    if (e >= 0 && e < E && local >= 0) {
+      const int pos = blk_base[(int64_t)(t / DISPATCH_TB) * E + e] + local;
+      if (pos < C) {
+        row = offset[e] + pos;
+        row_token[row] = t;
+        row_slot[row] = lane;
+      }
+    }
+    pair_row[p] = row;
+  }
+  int rows[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) rows[j] = __shfl(row, j, 64);
+
+  constexpr int VN = Vec<T>::N;
+  const int nvec = H / VN;
+  const T* src = x + (int64_t)t * H;
+  for (int v = lane; v < nvec; v += 64) {
+    const u32x4 val = ld16(src + (int64_t)v * VN);
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k && rows[j] >= 0) st16_nt(send_buf + (int64_t)rows[j] * H + (int64_t)v * VN, val);
+  }
+}
+
+}  // namespace
+
+int dispatch_num_blocks(int T) { return ceil_div_host(T, DISPATCH_TB); }
+
+hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const moe_layout_t& L, void* send_buf,
+                           int* blk_count, int* pair_local, hipStream_t stream) {
+  const int nblk = dispatch_num_blocks(L.T);
+  if (nblk > 0) dispatch_rank_kernel<<<nblk, DR_THREADS, 0, stream>>>(ids, L.T, L.k, L.E, blk_count, pair_local);
+  // with no tokens the scan still writes zero counts and offsets
+  dispatch_scan_kernel<<<1, DS_THREADS, 0, stream>>>(blk_count, nblk, L.E, L.C, L.expert_count, L.expert_kept,
+                                                     L.expert_overflow, L.expert_offset);
+  if (L.T == 0) return hipGetLastError();
+  const int blocks = ceil_div_host(L.T, 4);
+  if (xdt_bf16)
+    dispatch_scatter_kernel<bf16_t><<<blocks, 256, 0, stream>>>(
+        static_cast<const bf16_t*>(x), ids, L.T, L.H, L.k, L.E, L.C, blk_count, pair_local, L.expert_offset,
+        L.row_token, L.row_slot, L.pair_row, static_cast<bf16_t*>(send_buf));
+  else
+    dispatch_scatter_kernel<float><<<blocks, 256, 0, stream>>>(
+        static_cast<const float*>(x), ids, L.T, L.H, L.k, L.E, L.C, blk_count, pair_local, L.expert_offset,
+        L.row_token, L.row_slot, L.pair_row, static_cast<float*>(send_buf));
+  return hipGetLastError();
+}
+
+}  // namespace moe

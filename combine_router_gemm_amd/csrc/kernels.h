@@ -1,0 +1,43 @@
+// Host-side declarations of the kernel launchers (one translation unit per stage) used by the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+inline int ceil_div_host(int a, int b) { return (a + b - 1) / b; }
+inline int64_t ceil_div_host64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// ---- route ----
+int route_splits(int T, int H, int E, int num_cus);
+int route_k_split(int H, int splits);
+hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, const float* bias,
+                        int64_t bias_stride, int T, int H, int E, int k, float* logits, int* ids, float* wts,
+                        float* partial, int splits, hipStream_t stream);
+
+// ---- dispatch ----
+constexpr int DISPATCH_TB = 256;  // tokens per counting block
+int dispatch_num_blocks(int T);
+hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const moe_layout_t& L, void* send_buf,
+                           int* blk_count, int* pair_local, hipStream_t stream);
+
+// ---- expert MLP ----
+struct MlpTiles {
+  int BM;       // rows per tile (shared by both GEMMs; the plan is built for it)
+  int variant;  // kernel family, see mlp.hip
+};
+MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int xdt_bf16);
+size_t mlp_plan_ints(int El);
+hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
+                             const void* w_down, int F, void* out_buf, int* plan, int* perm, void* hbuf,
+                             const MlpTiles& tiles, int num_cus, hipStream_t stream);
+
+// ---- combine ----
+hipError_t launch_combine(const void* out_buf, int xdt_bf16, const moe_layout_t& L, const float* topk_w, void* y,
+                          hipStream_t stream);
+
+}  // namespace moe

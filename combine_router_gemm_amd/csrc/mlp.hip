@@ -1,0 +1,413 @@
+// Expert SwiGLU MLP as a persistent grouped GEMM over every local expert.
+//
+// The dispatched rows are multiplied by the expert weights with grouped GEMM kernels ("Enabling
+// trillion-parameter models on AWS EFA", section "MoE all-to-all через EFA"); one persistent GEMM
+// processes every expert of the rank without relaunching ("Mixture-of-experts acceleration through
+// overlap"). A row of global expert e uses local expert l = e mod El: the R rank segments of the send
+// buffer each hold rows for every local expert, and one GPU's share runs them all against its El weight
+// sets.
+//
+// Kernels:
+//   mlp_plan      one workgroup. M_l = sum_r kept[r*El + l]; prefix sums give each local expert's
+//                 first row in "plan order" (local expert major, then rank segment, then token) and
+//                 its first M-tile; perm[p] = send-buffer row of plan row p. Everything the GEMMs need
+//                 is derived on the device from the dispatch counts: no host synchronisation.
+//   mlp_gemm      persistent MFMA GEMM, C[p, n] = sum_k A[p, k] * B[n, k] ("NT": both operands are
+//                 K-contiguous, the nn.Linear [out, in] layout). Tiles are visited local expert major,
+//                 then N tile, then M tile, so workgroups running side by side share a weight slice;
+//                 the workgroup -> tile map groups consecutive tiles on one XCD (workgroups are dealt
+//                 to the 8 XCDs round robin, and each XCD has its own L2).
+//                 Gate/up pass: A rows gathered through perm from the send buffer, B = the gate and the
+//                 up rows of the same output columns, epilogue h = silu(g) * u (fp32) stored as xdt.
+//                 Down pass: A = h in plan order, epilogue stores to out_buf[perm[p]] as xdt.
+//   Operands are staged through LDS (global -> registers -> LDS, the next stage's global loads in
+//   flight while MFMAs run on the current one). bf16 uses v_mfma_f32_16x16x32_bf16, fp32 uses
+//   v_mfma_f32_16x16x4_f32; both accumulate in fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+// ------------------------------------------------------------------------------------------------
+// plan
+// ------------------------------------------------------------------------------------------------
+// plan layout (int32): [0] total M-tiles, [1] total rows, [2 .. 2+El] row start per local expert
+// (El+1 entries), [3+El .. 3+2El] M-tile start per local expert (El+1 entries).
+constexpr int PLAN_THREADS = 1024;
+
+__global__ __launch_bounds__(PLAN_THREADS) void mlp_plan_kernel(const int* __restrict__ kept,
+                                                               const int* __restrict__ offset, int E, int El,
+                                                               int BM, int* __restrict__ plan,
+                                                               int* __restrict__ perm) {
+  __shared__ int s_rows[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_tiles[MOE_MAX_EXPERTS + 1];
+  const int tid = threadIdx.x;
+  const int R = E / El;
+  if (tid < El) {
+    int m = 0;
+    for (int r = 0; r < R; ++r) m += kept[r * El + tid];
+    s_rows[tid] = m;
+    s_tiles[tid] = (m + BM - 1) / BM;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // El <= 512: a serial scan is a few microseconds at most and keeps the plan obviously ordered
+    int acc_r = 0, acc_t = 0;
+    for (int l = 0; l < El; ++l) {
+      const int m = s_rows[l], t = s_tiles[l];
+      s_rows[l] = acc_r;
+      s_tiles[l] = acc_t;
+      acc_r += m;
+      acc_t += t;
+    }
+    s_rows[El] = acc_r;
+    s_tiles[El] = acc_t;
+    plan[0] = acc_t;
+    plan[1] = acc_r;
+  }
+  __syncthreads();
+  int* row_start = plan + 2;
+  int* tile_start = plan + 3 + El;
+  for (int l = tid; l <= El; l += PLAN_THREADS) {
+    row_start[l] = s_rows[l];
+    tile_start[l] = s_tiles[l];
+  }
+  // perm: one thread per global expert e copies its kept rows into local expert (e mod El)'s range
+  for (int e = tid; e < E; e += PLAN_THREADS) {
+    const int l = e % El, r = e / El;
+    int dst = s_rows[l];
+    for (int rr = 0; rr < r; ++rr) dst += kept[rr * El + l];
+    const int src = offset[e];
+    const int n = kept[e];
+    for (int i = 0; i < n; ++i) perm[dst + i] = src + i;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// GEMM
+// ------------------------------------------------------------------------------------------------
+template <typename T>
+struct Mfma;
+
+// bf16: one v_mfma_f32_16x16x32_bf16 per 32-wide K chunk; lane l supplies 8 consecutive K of row l%16
+template <>
+struct Mfma<bf16_t> {
+  static __device__ __forceinline__ void step(f32x4& acc, const u32x4 (&a)[1], const u32x4 (&b)[1]) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[0]), __builtin_bit_cast(bf16x8, b[0]),
+                                                  acc, 0, 0, 0);
+  }
+  static constexpr int VPF = 1;  // 16-byte vectors per lane per 32-K fragment
+};
+
+// fp32: eight v_mfma_f32_16x16x4_f32 per 32-wide K chunk; step q takes K = (l/16)*8 + q, the same
+// assignment for A and B, so the eight steps cover the chunk once
+template <>
+struct Mfma<float> {
+  static __device__ __forceinline__ void step(f32x4& acc, const u32x4 (&a)[2], const u32x4 (&b)[2]) {
+    float fa[8], fb[8];
+    unpack(a[0], *reinterpret_cast<float(*)[4]>(&fa[0]));
+    unpack(a[1], *reinterpret_cast<float(*)[4]>(&fa[4]));
+    unpack(b[0], *reinterpret_cast<float(*)[4]>(&fb[0]));
+    unpack(b[1], *reinterpret_cast<float(*)[4]>(&fb[4]));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[q], fb[q], acc, 0, 0, 0);
+  }
+  static constexpr int VPF = 2;
+};
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+struct GemmArgs {
+  const void* A;        // activations: send_buf (gate/up) or h (down)
+  int lda;              // row length of A (= K)
+  const int* a_perm;    // gather map for A rows (gate/up) or nullptr (A in plan order)
+  const void* W;        // [El, ...] expert weights
+  int64_t w_stride;     // elements per expert
+  int K;
+  int N;                // output columns per expert (F for gate/up, H for down)
+  int up_offset;        // gate/up: row offset of the up half inside an expert's weights (= F)
+  void* Out;
+  int ldo;
+  const int* out_perm;  // scatter map for output rows (down) or nullptr (plan order)
+  const int* plan;
+  int El;
+};
+
+// BM x BN tile, BK-deep LDS stages, WM x WN waves. GATED: the B tile holds BN/2 gate rows then the
+// BN/2 up rows of the same output columns, and each wave owns matching gate and up accumulators.
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool GATED>
+__global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
+  constexpr int NTH = WM * WN * 64;
+  constexpr int VN = Vec<T>::N;           // elements per 16-byte vector
+  constexpr int PAD = 16 / sizeof(T);     // one vector of padding per LDS row
+  constexpr int LDR = BK + PAD;           // LDS row length (elements)
+  constexpr int VPR = BK / VN;            // vectors per tile row per stage
+  constexpr int A_VEC = BM * VPR / NTH;   // A vectors loaded per thread per stage
+  constexpr int B_VEC = BN * VPR / NTH;
+  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+  constexpr int TM = WTM / 16;
+  constexpr int TN = GATED ? (BN / 2 / WN) / 16 : WTN / 16;  // per half when gated
+  constexpr int NACC = GATED ? 2 * TN : TN;
+  constexpr int OUT_COLS = GATED ? BN / 2 : BN;  // output columns per tile
+  static_assert(BM * VPR % NTH == 0 && BN * VPR % NTH == 0, "loader must tile evenly");
+  static_assert(TM >= 1 && TN >= 1, "wave tile too small");
+  static_assert(BK % 32 == 0, "BK must be a multiple of the 32-wide MFMA chunk");
+
+  __shared__ __attribute__((aligned(16))) T As[BM * LDR];
+  __shared__ __attribute__((aligned(16))) T Bs[BN * LDR];
+
+  const T* __restrict__ A = static_cast<const T*>(args.A);
+  const T* __restrict__ W = static_cast<const T*>(args.W);
+  T* __restrict__ Out = static_cast<T*>(args.Out);
+  const int El = args.El;
+  const int* row_start = args.plan + 2;
+  const int* tile_start = args.plan + 3 + El;
+  const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
+  const int total = args.plan[0] * n_tiles;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous run of tile ids
+  const int G = gridDim.x;
+  int vb = blockIdx.x;
+  if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+
+  for (int tile = vb; tile < total; tile += G) {
+    // tile -> (local expert l, n tile, m tile): l is the last expert with tile_start[l]*n_tiles <= tile
+    int lo = 0, hi = El;  // invariant: tile_start[lo]*n_tiles <= tile < tile_start[hi]*n_tiles
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_start[mid] * n_tiles <= tile) lo = mid;
+      else hi = mid;
+    }
+    const int l = lo;
+    const int mt_l = tile_start[l + 1] - tile_start[l];
+    const int local = tile - tile_start[l] * n_tiles;
+    const int nt = local / mt_l, mt = local % mt_l;
+    const int p0 = row_start[l] + mt * BM;
+    const int m_rows = min(BM, row_start[l + 1] - p0);
+    const int n0 = nt * OUT_COLS;
+    const T* Wl = W + (int64_t)l * args.w_stride;
+
+    // per-thread source rows (fixed for the whole K loop)
+    const T* a_src[A_VEC];
+    int a_lds[A_VEC];
+#pragma unroll
+    for (int i = 0; i < A_VEC; ++i) {
+      const int idx = tid + i * NTH;
+      const int r = idx / VPR, c = (idx % VPR) * VN;
+      a_lds[i] = r * LDR + c;
+      if (r < m_rows) {
+        const int p = p0 + r;
+        const int src_row = args.a_perm ? args.a_perm[p] : p;
+        a_src[i] = A + (int64_t)src_row * args.lda + c;
+      } else {
+        a_src[i] = nullptr;
+      }
+    }
+    const T* b_src[B_VEC];
+    int b_lds[B_VEC];
+#pragma unroll
+    for (int i = 0; i < B_VEC; ++i) {
+      const int idx = tid + i * NTH;
+      const int r = idx / VPR, c = (idx % VPR) * VN;
+      b_lds[i] = r * LDR + c;
+      int wrow, ncol;
+      if (GATED) {
+        const int half = r / (BN / 2), rr = r % (BN / 2);
+        ncol = n0 + rr;
+        wrow = ncol + half * args.up_offset;
+      } else {
+        ncol = n0 + r;
+        wrow = ncol;
+      }
+      b_src[i] = ncol < args.N ? Wl + (int64_t)wrow * args.K + c : nullptr;
+    }
+
+    f32x4 acc[TM][NACC];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    u32x4 ra[A_VEC], rb[B_VEC];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    auto load_stage = [&](int k0) {
+#pragma unroll
+      for (int i = 0; i < A_VEC; ++i) {
+        const int kc = k0 + (a_lds[i] % LDR);
+        ra[i] = (a_src[i] && kc < args.K) ? ld16(a_src[i] + k0) : zero;
+      }
+#pragma unroll
+      for (int i = 0; i < B_VEC; ++i) {
+        const int kc = k0 + (b_lds[i] % LDR);
+        rb[i] = (b_src[i] && kc < args.K) ? ld16(b_src[i] + k0) : zero;
+      }
+    };
+
+    load_stage(0);
+    for (int k0 = 0; k0 < args.K; k0 += BK) {
+      __syncthreads();  // the previous stage's MFMA reads of LDS are done
+#pragma unroll
+      for (int i = 0; i < A_VEC; ++i) st16(&As[a_lds[i]], ra[i]);
+#pragma unroll
+      for (int i = 0; i < B_VEC; ++i) st16(&Bs[b_lds[i]], rb[i]);
+      __syncthreads();
+      if (k0 + BK < args.K) load_stage(k0 + BK);
+
+      const int fr = lane & 15;
+      const int fk = (lane >> 4) * 8;  // 8 consecutive K per lane inside each 32-wide chunk
+#pragma unroll
+      for (int kk = 0; kk < BK; kk += 32) {
+        u32x4 af[TM][Mfma<T>::VPF];
+        u32x4 bfg[NACC][Mfma<T>::VPF];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const T* pa = &As[(wm * WTM + i * 16 + fr) * LDR + kk + fk];
+#pragma unroll
+          for (int q = 0; q < Mfma<T>::VPF; ++q) af[i][q] = ld16(pa + q * VN);
+        }
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) {
+          int brow;
+          if (GATED) {
+            const int half = j / TN, jj = j % TN;
+            brow = half * (BN / 2) + wn * (BN / 2 / WN) + jj * 16 + fr;
+          } else {
+            brow = wn * WTN + j * 16 + fr;
+          }
+          const T* pb = &Bs[brow * LDR + kk + fk];
+#pragma unroll
+          for (int q = 0; q < Mfma<T>::VPF; ++q) bfg[j][q] = ld16(pb + q * VN);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < NACC; ++j) Mfma<T>::step(acc[i][j], af[i], bfg[j]);
+      }
+    }
+
+    // epilogue: lane l holds column l%16 and rows 4*(l/16) + r of each 16x16 accumulator
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int cl = GATED ? wn * (BN / 2 / WN) + j * 16 + (lane & 15) : wn * WTN + j * 16 + (lane & 15);
+        const int col = n0 + cl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
+          if (row < m_rows && col < args.N) {
+            float v;
+            if (GATED) v = silu_f32(acc[i][j][r]) * acc[i][j + TN][r];
+            else v = acc[i][j][r];
+            const int p = p0 + row;
+            const int orow = args.out_perm ? args.out_perm[p] : p;
+            Out[(int64_t)orow * args.ldo + col] = from_f32<T>(v);
+          }
+        }
+      }
+    }
+    __syncthreads();  // LDS is reused by the next tile
+  }
+}
+
+template <typename T, int BM, int BN, int BK, int WM, int WN, bool GATED>
+void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
+  mlp_gemm_kernel<T, BM, BN, BK, WM, WN, GATED><<<grid, WM * WN * 64, 0, stream>>>(a);
+}
+
+// workgroups per CU for the persistent grid
+constexpr int WG_PER_CU = 2;
+
+int persistent_grid(int64_t max_tiles, int num_cus) {
+  int64_t g = (int64_t)num_cus * WG_PER_CU;
+  if (max_tiles < g) g = max_tiles;
+  if (g >= 8) g &= ~7ll;  // a multiple of the XCD count keeps the XCD-aware order exact
+  return (int)(g > 0 ? g : 1);
+}
+
+}  // namespace
+
+size_t mlp_plan_ints(int El) { return 2 + 2 * (size_t)(El + 1); }
+
+// variant 0: bf16 prefill tiles, 1: bf16 decode tiles (few rows per expert), 2: fp32
+MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int xdt_bf16) {
+  if (!xdt_bf16) return MlpTiles{32, 2};
+  const int64_t per_expert = El > 0 ? rows_max / El : rows_max;
+  if (per_expert >= 128) return MlpTiles{128, 0};
+  return MlpTiles{32, 1};
+}
+
+hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
+                             const void* w_down, int F, void* out_buf, int* plan, int* perm, void* hbuf,
+                             const MlpTiles& tiles, int num_cus, hipStream_t stream) {
+  const int El = L.E / L.R;
+  const int H = L.H;
+  mlp_plan_kernel<<<1, PLAN_THREADS, 0, stream>>>(L.expert_kept, L.expert_offset, L.E, El, tiles.BM, plan, perm);
+
+  const int64_t rows_max = moe_rows_max(L.T, L.k, L.E, L.C);
+  const int64_t max_mtiles = ceil_div_host64(rows_max, tiles.BM) + El;
+
+  GemmArgs gu{};
+  gu.A = send_buf;
+  gu.lda = H;
+  gu.a_perm = perm;
+  gu.W = w_gate_up;
+  gu.w_stride = (int64_t)2 * F * H;
+  gu.K = H;
+  gu.N = F;
+  gu.up_offset = F;
+  gu.Out = hbuf;
+  gu.ldo = F;
+  gu.out_perm = nullptr;
+  gu.plan = plan;
+  gu.El = El;
+
+  GemmArgs dn{};
+  dn.A = hbuf;
+  dn.lda = F;
+  dn.a_perm = nullptr;
+  dn.W = w_down;
+  dn.w_stride = (int64_t)H * F;
+  dn.K = F;
+  dn.N = H;
+  dn.up_offset = 0;
+  dn.Out = out_buf;
+  dn.ldo = H;
+  dn.out_perm = perm;
+  dn.plan = plan;
+  dn.El = El;
+
+  switch (tiles.variant) {
+    case 0: {  // bf16, many rows per expert: 128x128 tiles, 2x2 waves of 64x64
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 64), num_cus);
+      launch_gemm<bf16_t, 128, 128, 64, 2, 2, true>(gu, g1, stream);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 128), num_cus);
+      launch_gemm<bf16_t, 128, 128, 64, 2, 2, false>(dn, g2, stream);
+      break;
+    }
+    case 1: {  // bf16, few rows per expert: stream the weights with 32-row tiles
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 64), num_cus);
+      launch_gemm<bf16_t, 32, 128, 64, 1, 4, true>(gu, g1, stream);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 64), num_cus);
+      launch_gemm<bf16_t, 32, 64, 64, 1, 4, false>(dn, g2, stream);
+      break;
+    }
+    default: {  // fp32
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus);
+      launch_gemm<float, 32, 64, 32, 1, 2, true>(gu, g1, stream);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 64), num_cus);
+      launch_gemm<float, 32, 64, 32, 1, 2, false>(dn, g2, stream);
+      break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

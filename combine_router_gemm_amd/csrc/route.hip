@@ -1,0 +1,296 @@
+// Router: logits = x W_r^T (+ bias) in fp32, then per-token top-k and softmax over the k selected.
+//
+// The router is a small linear layer scoring every expert; the k best experts are chosen and their
+// weights come from the router's distribution ("Efficient and portable mixture-of-experts
+// communication", section "Introductie").
+//
+// Kernel 1 (route_gemm): split-K fp32 MFMA GEMM. Grid (token tiles, expert tiles, K splits); each
+//   workgroup writes an fp32 partial [T, E] for its K range. x is widened to fp32 exactly (bf16 is the
+//   top half of an fp32 word), so products are the fp32 products of the inputs.
+// Kernel 2 (route_topk): sums the K-split partials in a fixed order (deterministic), adds the bias,
+//   (with a single split the partial buffer is the logits buffer itself, read then overwritten in place),
+//   writes the logits and selects the top-k per token with a lane-group arg-max: G lanes per token,
+//   each holding E/G logits, k rounds of a butterfly max over (value desc, expert id asc).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int RG_BM = 64;   // tokens per tile
+constexpr int RG_BN = 64;   // experts per tile
+constexpr int RG_BK = 32;   // K per LDS stage
+constexpr int RG_LDS = RG_BK + 4;  // padded LDS row (floats): 144-byte rows keep b128 reads conflict-free
+
+// Load 8 consecutive elements of row `r`, K offset `kc`, widened to fp32 (zero outside the matrix).
+template <typename T>
+__device__ __forceinline__ void load8_f32(const T* base, int64_t ld, int r, int nrows, int kc, int kend,
+                                          float (&o)[8]);
+
+template <>
+__device__ __forceinline__ void load8_f32<float>(const float* base, int64_t ld, int r, int nrows, int kc,
+                                                 int kend, float (&o)[8]) {
+  if (r < nrows && kc < kend) {
+    const float* p = base + (int64_t)r * ld + kc;
+    float a[4], b[4];
+    unpack(ld16(p), a);
+    unpack(ld16(p + 4), b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] = a[i];
+      o[4 + i] = b[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8_f32<bf16_t>(const bf16_t* base, int64_t ld, int r, int nrows, int kc,
+                                                  int kend, float (&o)[8]) {
+  if (r < nrows && kc < kend) {
+    unpack(ld16(base + (int64_t)r * ld + kc), o);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  }
+}
+
+// grid: (ceil(T/64), ceil(E/64), splits); block 256 = 4 waves in 2x2, each wave a 32x32 output tile.
+template <typename TX>
+__global__ __launch_bounds__(256) void route_gemm_kernel(const TX* __restrict__ x, const float* __restrict__ w,
+                                                         int T, int H, int E, int k_split,
+                                                         float* __restrict__ partial) {
+  __shared__ float As[RG_BM][RG_LDS];
+  __shared__ float Bs[RG_BN][RG_LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * RG_BM;
+  const int e0 = blockIdx.y * RG_BN;
+  const int kbeg = blockIdx.z * k_split;
+  const int kend = min(H, kbeg + k_split);
+
+  // loader: 64 rows x 32 K = 256 groups of 8 -> one group per thread for each matrix
+  const int lr = tid >> 2;        // row in tile
+  const int lk = (tid & 3) * 8;   // K offset in stage
+
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float ra[8], rb[8];
+  const TX* xa = x + (int64_t)t0 * H;
+  const float* wb = w + (int64_t)e0 * H;
+  load8_f32<TX>(xa, H, lr, T - t0, kbeg + lk, kend, ra);
+  load8_f32<float>(wb, H, lr, E - e0, kbeg + lk, kend, rb);
+
+  for (int k0 = kbeg; k0 < kend; k0 += RG_BK) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      As[lr][lk + i] = ra[i];
+      Bs[lr][lk + i] = rb[i];
+    }
+    __syncthreads();
+    if (k0 + RG_BK < kend) {
+      load8_f32<TX>(xa, H, lr, T - t0, k0 + RG_BK + lk, kend, ra);
+      load8_f32<float>(wb, H, lr, E - e0, k0 + RG_BK + lk, kend, rb);
+    }
+    // lane l supplies row (l % 16) and K = (l / 16) * 8 + i for MFMA step i; A and B use the same
+    // K assignment, so the 8 steps together cover the 32-wide stage exactly once.
+    const int fr = lane & 15;
+    const int fk = (lane >> 4) * 8;
+    float af[2][8], bfr[2][8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float* pa = &As[wm * 32 + i * 16 + fr][fk];
+      const float* pb = &Bs[wn * 32 + i * 16 + fr][fk];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        af[i][q] = pa[q];
+        bfr[i][q] = pb[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i][q], bfr[j][q], acc[i][j], 0, 0, 0);
+  }
+
+  // C fragment: lane l holds column (l % 16), rows 4 * (l / 16) + r
+  float* out = partial + (int64_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = e0 + wn * 32 + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = t0 + wm * 32 + i * 16 + (lane >> 4) * 4 + r;
+        if (row < T && col < E) out[(int64_t)row * E + col] = acc[i][j][r];
+      }
+    }
+}
+
+// (value, id) ordering of the selection: larger value first, then lower id. NaN never wins a
+// comparison, so it is treated as -inf.
+__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
+  return (v > bv) || (v == bv && e < be);
+}
+
+// G lanes per token (power of two, 8..64), V = ceil(E / G) logits per lane, expert of lane g's
+// i-th value is i * G + g.
+template <int G>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, int splits,
+                                                         const float* __restrict__ bias, int64_t bias_stride,
+                                                         int T, int E, int k, float* logits,
+                                                         int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  // G < 64 is only chosen when E <= G (one logit per lane); G == 64 covers E <= 512 (8 per lane)
+  constexpr int VMAX = G < 64 ? 1 : MOE_MAX_EXPERTS / 64;
+  const int g = threadIdx.x & (G - 1);
+  const int t = (blockIdx.x * blockDim.x + threadIdx.x) / G;
+  const bool live = t < T;
+  const int V = (E + G - 1) / G;
+
+  float val[VMAX];
+  bool taken[VMAX];
+#pragma unroll
+  for (int i = 0; i < VMAX; ++i) {
+    val[i] = -INFINITY;
+    taken[i] = true;
+    const int e = i * G + g;
+    if (i < V && e < E && live) {
+      const int64_t idx = (int64_t)t * E + e;
+      float s = partial[idx];
+      for (int sp = 1; sp < splits; ++sp) s += partial[(int64_t)sp * T * E + idx];
+      if (bias) s += bias[(int64_t)t * bias_stride + e];
+      logits[idx] = s;
+      s = s + 0.0f;                     // -0 -> +0: equal values compare equal either way
+      val[i] = (s == s) ? s : -INFINITY;  // NaN ranks as -inf
+      taken[i] = false;
+    }
+  }
+
+  float sel_v[MOE_MAX_TOPK];
+  int sel_e[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j < k) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i) {
+        const int e = i * G + g;
+        if (!taken[i] && better(val[i], e, bv, be)) {
+          bv = val[i];
+          be = e;
+        }
+      }
+#pragma unroll
+      for (int off = G / 2; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, G);
+        const int oe = __shfl_xor(be, off, G);
+        if (better(ov, oe, bv, be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      sel_v[j] = bv;
+      sel_e[j] = be;
+      if ((be & (G - 1)) == g) {
+        const int ii = be / G;
+#pragma unroll
+        for (int i = 0; i < VMAX; ++i)
+          if (i == ii) taken[i] = true;
+      }
+    }
+  }
+
+  if (live && g < k) {
+    // softmax over the k selected logits (slot 0 holds the largest)
+    const float m = sel_v[0];
+    float sum = 0.f, mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        const float z = expf(sel_v[j] - m);
+        sum += z;
+        if (j == g) mine = z;
+      }
+    }
+    int myid = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j == g) myid = sel_e[j];
+    topk_ids[(int64_t)t * k + g] = myid;
+    topk_w[(int64_t)t * k + g] = mine / sum;
+  }
+}
+
+}  // namespace
+
+// Host-side planning of the split-K factor: enough workgroups to cover the chip twice, each split at
+// least 256 K-elements long and a multiple of the 32-wide stage.
+int route_splits(int T, int H, int E, int num_cus) {
+  const int tiles = ceil_div_host(T, RG_BM) * ceil_div_host(E, RG_BN);
+  int s = ceil_div_host(2 * num_cus, tiles > 0 ? tiles : 1);
+  const int smax = H / 256 > 0 ? H / 256 : 1;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  return s;
+}
+
+int route_k_split(int H, int splits) {
+  int ks = ceil_div_host(H, splits);
+  return ceil_div_host(ks, RG_BK) * RG_BK;
+}
+
+hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, const float* bias,
+                        int64_t bias_stride, int T, int H, int E, int k, float* logits, int* ids, float* wts,
+                        float* partial, int splits, hipStream_t stream) {
+  const int k_split = route_k_split(H, splits);
+  const int nsplit = ceil_div_host(H, k_split);
+  dim3 grid(ceil_div_host(T, RG_BM), ceil_div_host(E, RG_BN), nsplit);
+  if (xdt_bf16)
+    route_gemm_kernel<bf16_t><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H, E,
+                                                        k_split, partial);
+  else
+    route_gemm_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), w_router, T, H, E, k_split,
+                                                       partial);
+  // lane-group size: smallest power of two >= E, between 8 and 64
+  int G = 8;
+  while (G < E && G < 64) G *= 2;
+  const int threads = 256;
+  const int blocks = ceil_div_host(T * G, threads);
+  switch (G) {
+    case 8:
+      route_topk_kernel<8><<<blocks, threads, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
+                                                          ids, wts);
+      break;
+    case 16:
+      route_topk_kernel<16><<<blocks, threads, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
+                                                           ids, wts);
+      break;
+    case 32:
+      route_topk_kernel<32><<<blocks, threads, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
+                                                           ids, wts);
+      break;
+    default:
+      route_topk_kernel<64><<<blocks, threads, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
+                                                           ids, wts);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,192 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer hot path: one GPU's share of an expert-parallel
+ * Mixture-of-Experts layer, run as four calls on one HIP stream:
+ *
+ *   moe_route      -> router logits, top-k experts and their weights per token
+ *   moe_dispatch   -> per-expert histogram, prefix scan with a capacity limit, stable scatter of
+ *                     token rows into contiguous, destination-rank-aligned per-expert rows
+ *   moe_expert_mlp -> per-expert SwiGLU MLP over the dispatched rows (grouped bf16 MFMA GEMM)
+ *   moe_combine    -> router-weighted sum of each token's expert outputs, back in token order
+ *
+ * Sources (cited by page title and section):
+ *   [EPM] "Efficient and portable mixture-of-experts communication" (Perplexity, 2025)
+ *   [EFA] "Enabling trillion-parameter models on AWS EFA" (Perplexity, 2025)
+ *   [OVL] "Mixture-of-experts acceleration through overlap" (thecoregrid.dev)
+ *   [EPB] "80. MoE Expert Parallel Benchmark" (datawhalechina llm-algo-leetcode)
+ *   [DMoE] "DistributedMoE" (README)
+ *
+ * Conventions shared by every call:
+ *   - All pointers except `moe_layout_t*` itself are DEVICE pointers, owned by the caller. The library
+ *     allocates nothing, keeps no state between calls and never synchronises with the host; each
+ *     call only enqueues kernels on `stream` (NULL = the default stream) and returns.
+ *   - Row-major layouts, 32-bit indices. Activations and expert weights share one type `xdt`
+ *     (MOE_F32 or MOE_BF16); the router weight, bias, logits and routing weights are fp32.
+ *   - Return value: MOE_OK, or a negative status. Arguments are validated on the host before any
+ *     HIP call; on MOE_ERR_INVALID / MOE_ERR_UNSUPPORTED nothing was enqueued. MOE_ERR_HIP means a
+ *     launch failed (hipGetLastError); earlier kernels of the same call may have run.
+ *   - Same inputs give bitwise-identical outputs: no floating-point atomics anywhere.
+ *   - Calls on different streams with disjoint buffers are independent.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = -1,     /* null pointer, out-of-range size, inconsistent layout */
+  MOE_ERR_UNSUPPORTED = -2, /* a shape or dtype the kernels do not handle (e.g. H % 8 != 0) */
+  MOE_ERR_HIP = -3          /* a kernel launch failed */
+};
+
+/* Limits checked on the host. */
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_TOPK 8
+
+/* Text for a status code (static storage). */
+const char* moe_status_string(int status);
+
+/*
+ * Layout descriptor of the per-rank send buffers ([EFA] "Диспетчеризация и комбинирование": counts
+ * per expert, a cumulative sum gives the offsets, tokens are packed into contiguous per-peer send
+ * buffers; [OVL]: each tile belongs to one destination rank, so a transfer is one contiguous write;
+ * [EPM] "Dispatch": the receiver keeps (source rank, expert, token) for the combine).
+ *
+ * The caller fills the scalars and allocates the arrays (device memory, int32); moe_dispatch fills
+ * the arrays. E experts are split over R destination ranks, El = E / R per rank, expert e on rank
+ * e / El. Rows are ordered by expert id and, inside an expert, by token (stable). Rank r's segment is
+ * rows [expert_offset[r*El], expert_offset[(r+1)*El]). Rows >= expert_offset[E] are unspecified.
+ *
+ *   expert_count[E]     tokens routed to each expert (the router histogram)
+ *   expert_kept[E]      min(count, C)                      ([EPB] Step 2)
+ *   expert_overflow[E]  max(count - C, 0)                  ([EPB] Step 2)
+ *   expert_offset[E+1]  exclusive prefix sum of kept; [E] = total rows
+ *   row_token[rows_max] source token of each row
+ *   row_slot[rows_max]  k-slot of each row
+ *   pair_row[T*k]       row of pair (t, j), or -1 if the pair was dropped by the capacity limit
+ *
+ * rows_max = moe_rows_max(T, k, E, C) = min(T*k, E*C) bounds the row count from host scalars alone.
+ */
+typedef struct moe_layout {
+  int32_t T;  /* tokens */
+  int32_t k;  /* experts per token, 1..MOE_MAX_TOPK */
+  int32_t E;  /* experts, 1..MOE_MAX_EXPERTS */
+  int32_t R;  /* destination ranks, E % R == 0 */
+  int32_t C;  /* per-expert capacity, >= 0 (an integer: the caller rounds cf*T*k/E) */
+  int32_t H;  /* hidden size, % 8 == 0 */
+  int32_t* expert_count;
+  int32_t* expert_kept;
+  int32_t* expert_overflow;
+  int32_t* expert_offset;
+  int32_t* row_token;
+  int32_t* row_slot;
+  int32_t* pair_row;
+} moe_layout_t;
+
+/* min(T*k, E*C): the most rows dispatch can produce. Negative arguments give 0. */
+int64_t moe_rows_max(int T, int k, int E, int C);
+
+/*
+ * moe_route -- router scores and top-k selection.
+ * [EPM] "Introductie": the router is a small linear layer giving a probability distribution over the
+ * experts; the top-K experts are chosen and the output is a weighted average with weights derived
+ * from that distribution. [EFA] "Введение": a small routing linear layer picks the experts.
+ *
+ *   x            [T, H] activations (xdt)
+ *   w_router     [E, H] fp32 router weight
+ *   logit_bias   NULL, or fp32 bias added to the logits; row t reads logit_bias[t*bias_row_stride + e]
+ *                (stride 0: one [E] row for all tokens; stride E: a [T, E] matrix)
+ *   logits       [T, E] fp32 output: sum_h x[t,h] * w_router[e,h] + bias, accumulated in fp32
+ *   topk_ids     [T, k] int32 output: the k largest logits, descending, equal logits ordered by the
+ *                lower expert id, -0 == +0 (slot 0 = best)
+ *   topk_w       [T, k] fp32 output: softmax over the k selected logits (sums to 1)
+ *   workspace    device scratch of at least moe_route_workspace_bytes(T, H, E) bytes
+ * Requires 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS, H % 8 == 0, T >= 0 (T == 0 is a
+ * no-op). NaN/Inf logits give unspecified ids.
+ */
+int moe_route(const void* x, moe_dtype_t xdt, const float* w_router, const float* logit_bias,
+              int64_t bias_row_stride, int T, int H, int E, int k, float* logits, int32_t* topk_ids,
+              float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of scratch `workspace` moe_route needs for (T, H, E): fp32 partial sums when the H
+ * reduction is split across workgroups (0 when it is not; workspace may then be NULL). */
+size_t moe_route_workspace_bytes(int T, int H, int E);
+
+/* Bytes of scratch `workspace` moe_dispatch needs for (T, k, E). */
+size_t moe_dispatch_workspace_bytes(int T, int k, int E);
+
+/*
+ * moe_dispatch -- partition (token, slot) pairs by expert into contiguous per-expert rows.
+ * [EFA] "Диспетчеризация и комбинирование": per-expert counts by atomic accumulation in on-chip
+ * memory, a cumulative sum of the counts gives the offsets, tokens are packed into contiguous send
+ * buffers. [EPB] Step 2: capacity is the per-expert limit of one step; overflow = max(assigned -
+ * capacity, 0). [EPM] "Dispatch": tokens are regrouped into contiguous per-expert buffers that feed
+ * the grouped GEMM, and (rank, expert, token) is kept per row for the combine.
+ *
+ * Pairs are admitted first come first served in row-major (t, j) order: pair (t, j) of expert e is
+ * kept iff fewer than C earlier pairs chose e; kept rows are bit copies of x[t].
+ *   x          [T, H] activations (xdt); T, H, k, E, R, C are read from `layout`
+ *   topk_ids   [T, k] int32 expert ids (distinct within a token, in [0, E))
+ *   layout     host struct with scalars set and device arrays allocated (see moe_layout_t)
+ *   send_buf   [rows_max, H] (xdt) output rows
+ *   workspace  device scratch of at least moe_dispatch_workspace_bytes(T, k, E) bytes
+ * Ids outside [0, E) give unspecified output (they are not written anywhere out of bounds).
+ */
+int moe_dispatch(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const moe_layout_t* layout,
+                 void* send_buf, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of scratch `workspace` moe_expert_mlp needs for this layout and FFN width. */
+size_t moe_expert_mlp_workspace_bytes(int T, int k, int E, int R, int C, int F, moe_dtype_t xdt);
+
+/*
+ * moe_expert_mlp -- per-expert SwiGLU MLP on the dispatched rows, as a grouped GEMM.
+ * [EFA] "MoE all-to-all через EFA": grouped GEMM kernels multiply the regrouped tokens by the expert
+ * weights. [OVL]: one persistent GEMM processes every expert of the rank without relaunching.
+ * [DMoE] "Результаты": grouped GEMM helps most when many experts are active.
+ *
+ * A row of global expert e uses local expert l = e mod El (El = E / R):
+ *   g = x Wg[l]^T, u = x Wu[l]^T (fp32 accumulate), h = silu(g) * u stored as xdt,
+ *   out = h Wd[l]^T (fp32 accumulate) stored as xdt.
+ *   send_buf   [rows_max, H] rows written by moe_dispatch (xdt)
+ *   layout     the layout moe_dispatch filled (expert_kept / expert_offset are read on the device)
+ *   w_gate_up  [El, 2F, H] (xdt): rows 0..F-1 are Wg, rows F..2F-1 are Wu (nn.Linear [out, in])
+ *   w_down     [El, H, F] (xdt)
+ *   out_buf    [rows_max, H] (xdt) output, row-aligned with send_buf; rows >= total unspecified
+ *   workspace  device scratch of at least moe_expert_mlp_workspace_bytes(...) bytes
+ * Requires H % 8 == 0 and F % 8 == 0. bf16 runs on bf16 MFMA, fp32 on fp32 MFMA.
+ */
+int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* layout,
+                   const void* w_gate_up, const void* w_down, int F, void* out_buf, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_combine -- router-weighted sum back in token order.
+ * [EPM] "Combine": the payloads are read from the per-expert buffers, the routing table says which
+ * buffer to read and which weight each expert gets, and the result is written to caller-allocated
+ * tensors. [EFA] "Буферы отправки и получения": combine reads the receive buffer and computes the
+ * weighted average of the tokens into the output tensors.
+ *
+ *   y[t] = sum over kept slots j, ascending, of topk_w[t,j] * out_buf[pair_row[t,j]],
+ *   accumulated in fp32 and rounded once to xdt; a token with every pair dropped gets y[t] = 0.
+ *   out_buf  [rows_max, H] (xdt) expert outputs, row-aligned with send_buf
+ *   layout   the layout moe_dispatch filled (pair_row is read on the device)
+ *   topk_w   [T, k] fp32 routing weights
+ *   y        [T, H] (xdt) output
+ */
+int moe_combine(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout,
+                const float* topk_w, void* y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,158 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol include/moe.h declares,
+computes sizes on the host, and rejects invalid arguments before any HIP call.
+
+Also checks that the oracle and the HIP path stay independent (neither imports the other).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_router_gemm_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED = -1, -2
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails before any use
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.library_path()):
+        pytest.skip("HIP library not built (python -m combine_router_gemm_amd.build)")
+    return moe.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert set(names) == set(moe.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert moe.moe_status_string(0) == "ok"
+    assert moe.moe_status_string(-1) == "invalid argument"
+    assert moe.moe_status_string(-2) == "unsupported shape or dtype"
+    assert moe.moe_status_string(-3) == "HIP launch error"
+
+
+def test_rows_max(lib):
+    assert moe.moe_rows_max(4096, 8, 256, 128) == 32768
+    assert moe.moe_rows_max(128, 8, 384, 4) == 1024
+    assert moe.moe_rows_max(16384, 8, 256, 512) == 131072
+    assert moe.moe_rows_max(256, 2, 8, 80) == 512
+    assert moe.moe_rows_max(10, 2, 3, 2) == 6
+    assert moe.moe_rows_max(0, 2, 8, 5) == 0
+    assert moe.moe_rows_max(10, 2, 8, 0) == 0
+
+
+def test_workspace_sizes(lib):
+    assert moe.moe_dispatch_workspace_bytes(4096, 8, 256) >= (16 * 256 + 4096 * 8) * 4
+    assert moe.moe_dispatch_workspace_bytes(0, 8, 256) == 0
+    # h [rows_max, F] bf16 dominates the MLP workspace
+    assert moe.moe_expert_mlp_workspace_bytes(4096, 8, 256, 8, 128, 2048, moe.MOE_BF16) >= 32768 * 2048 * 2
+    assert moe.moe_expert_mlp_workspace_bytes(256, 2, 8, 1, 80, 256, moe.MOE_F32) >= 512 * 256 * 4
+    # the router needs scratch only when the H reduction is split
+    assert moe.moe_route_workspace_bytes(16384, 7168, 256) == 0
+    assert moe.moe_route_workspace_bytes(128, 4096, 8) > 0
+
+
+def _route(lib, **kw):
+    a = dict(x=FAKE, xdt=moe.MOE_BF16, w=FAKE, bias=None, stride=0, T=16, H=64, E=8, k=2, logits=FAKE,
+             ids=FAKE, wts=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.moe_route(a["x"], a["xdt"], a["w"], a["bias"], a["stride"], a["T"], a["H"], a["E"], a["k"],
+                         a["logits"], a["ids"], a["wts"], a["ws"], a["wsb"], None)
+
+
+def test_route_rejects_invalid_arguments(lib):
+    assert _route(lib, k=0) == MOE_ERR_INVALID
+    assert _route(lib, k=9, E=16) == MOE_ERR_INVALID
+    assert _route(lib, k=4, E=3) == MOE_ERR_INVALID
+    assert _route(lib, E=513) == MOE_ERR_INVALID
+    assert _route(lib, T=-1) == MOE_ERR_INVALID
+    assert _route(lib, H=12) == MOE_ERR_UNSUPPORTED
+    assert _route(lib, xdt=7) == MOE_ERR_UNSUPPORTED
+    assert _route(lib, x=None) == MOE_ERR_INVALID
+    assert _route(lib, ids=None) == MOE_ERR_INVALID
+    assert _route(lib, bias=FAKE, stride=-1) == MOE_ERR_INVALID
+    # needs scratch (split reduction) but none given
+    assert _route(lib, T=128, H=4096, E=8, ws=None, wsb=0) == MOE_ERR_INVALID
+    # T == 0 is a no-op that succeeds without touching anything
+    assert _route(lib, T=0, x=None, logits=None, ids=None, wts=None) == 0
+
+
+def _layout(**kw):
+    d = dict(T=16, k=2, E=8, R=1, C=4, H=64)
+    d.update(kw)
+    arr = [FAKE.value] * 7
+    for name in kw.get("null", ()):
+        arr[["expert_count", "expert_kept", "expert_overflow", "expert_offset", "row_token", "row_slot",
+             "pair_row"].index(name)] = None
+    d.pop("null", None)
+    return moe._CLayout(d["T"], d["k"], d["E"], d["R"], d["C"], d["H"], *arr)
+
+
+def test_dispatch_rejects_invalid_arguments(lib):
+    def call(L, xdt=moe.MOE_BF16, x=FAKE, ids=FAKE, sb=FAKE, ws=FAKE, wsb=1 << 30):
+        return lib.moe_dispatch(x, xdt, ids, ctypes.byref(L), sb, ws, wsb, None)
+    assert lib.moe_dispatch(FAKE, moe.MOE_BF16, FAKE, None, FAKE, FAKE, 1 << 30, None) == MOE_ERR_INVALID
+    assert call(_layout(E=10, R=3)) == MOE_ERR_INVALID          # E % R != 0
+    assert call(_layout(k=9, E=16)) == MOE_ERR_INVALID
+    assert call(_layout(C=-1)) == MOE_ERR_INVALID
+    assert call(_layout(H=60)) == MOE_ERR_UNSUPPORTED
+    assert call(_layout(), xdt=3) == MOE_ERR_UNSUPPORTED
+    assert call(_layout(null=("pair_row",))) == MOE_ERR_INVALID
+    assert call(_layout(null=("expert_offset",))) == MOE_ERR_INVALID
+    assert call(_layout(), sb=None) == MOE_ERR_INVALID
+    assert call(_layout(), ws=None) == MOE_ERR_INVALID
+    assert call(_layout(), wsb=16) == MOE_ERR_INVALID
+
+
+def test_mlp_and_combine_reject_invalid_arguments(lib):
+    L = _layout()
+    assert lib.moe_expert_mlp(FAKE, moe.MOE_BF16, ctypes.byref(L), FAKE, FAKE, 0, FAKE, FAKE, 1 << 30,
+                              None) == MOE_ERR_INVALID
+    assert lib.moe_expert_mlp(FAKE, moe.MOE_BF16, ctypes.byref(L), FAKE, FAKE, 12, FAKE, FAKE, 1 << 30,
+                              None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_mlp(FAKE, moe.MOE_BF16, ctypes.byref(L), None, FAKE, 64, FAKE, FAKE, 1 << 30,
+                              None) == MOE_ERR_INVALID
+    assert lib.moe_expert_mlp(FAKE, moe.MOE_BF16, ctypes.byref(L), FAKE, FAKE, 64, FAKE, FAKE, 8,
+                              None) == MOE_ERR_INVALID
+    assert lib.moe_combine(FAKE, moe.MOE_BF16, ctypes.byref(L), None, FAKE, None) == MOE_ERR_INVALID
+    assert lib.moe_combine(FAKE, 5, ctypes.byref(L), FAKE, FAKE, None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine(FAKE, moe.MOE_BF16, ctypes.byref(_layout(E=0)), FAKE, FAKE, None) == MOE_ERR_INVALID
+
+
+def _py_sources(folder):
+    for dirpath, _, files in os.walk(os.path.join(ROOT, folder)):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                yield os.path.join(dirpath, f)
+
+
+def test_oracle_and_hip_path_are_independent():
+    for path in _py_sources("oracle"):
+        assert "combine_router_gemm_amd" not in open(path).read(), path
+    for path in _py_sources("combine_router_gemm_amd"):
+        text = open(path).read()
+        assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), path
+    for path in _py_sources("moe_workloads"):
+        text = open(path).read()
+        assert not re.search(r"^\s*(import|from)\s+(oracle|combine_router_gemm_amd)\b", text, flags=re.M), path
+
+
+def test_library_missing_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "_PKG", str(tmp_path))
+    with pytest.raises(moe.MoeError, match="missing"):
+        moe.load_library()
