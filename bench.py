@@ -35,7 +35,56 @@ def parse():
     ap.add_argument("--workload", default=None,
                     help="workload name or number (default: mixtral8x7b-decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (3 times), the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters, and exit")
     return ap.parse_args()
+
+
+MLP_SOURCES = ("combine_router_gemm_amd/csrc/mlp.hip", "combine_router_gemm_amd/csrc/common.h")
+
+
+def mlp_source_digest() -> str:
+    """sha256 over the expert-MLP kernel sources: counters taken on other sources no longer apply."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in MLP_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per moe_expert_mlp call from the committed counter summary of this workload, or None
+    if there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"expert_mlp_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                key, _, val = line[2:].partition(":")
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("source_sha256") != mlp_source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mib: int) -> None:
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device-to-device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
+                      "copies": 3}), flush=True)
 
 
 def pick_workload(name):
@@ -108,6 +157,10 @@ def main():
               f"multi-GPU path; the single-GPU figure is the per-GPU share.", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
+
     import torch
 
     import combine_router_gemm_amd as moe
@@ -133,7 +186,7 @@ def main():
     out_buf = torch.empty_like(send_buf)
     y = torch.empty(T, H, dtype=x.dtype, device=dev)
     xdt = moe.MOE_BF16 if x.dtype == torch.bfloat16 else moe.MOE_F32
-    ws_route = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E)), dtype=torch.uint8, device=dev)
+    ws_route = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E, xdt)), dtype=torch.uint8, device=dev)
     ws_disp = torch.empty(max(1, moe.moe_dispatch_workspace_bytes(T, k, E)), dtype=torch.uint8, device=dev)
     ws_mlp = torch.empty(max(1, moe.moe_expert_mlp_workspace_bytes(T, k, E, R, C, F, xdt)), dtype=torch.uint8,
                          device=dev)
@@ -199,6 +252,7 @@ def main():
         achieved = ab["mlp"] / mlp_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+    roof["traffic"] = measured_traffic(cfg.name)
     roof["kernel"] = "moe_expert_mlp (grouped GEMM: plan + gate/up + down launches)"
     roof["algorithmic_bytes"] = ab["mlp"]
     roof["algorithmic_flops"] = ab["mlp_flops"]

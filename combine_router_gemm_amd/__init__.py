@@ -66,7 +66,7 @@ def load_library():
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_rows_max.argtypes = [i32, i32, i32, i32]
     lib.moe_rows_max.restype = i64
-    lib.moe_route_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.moe_route_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.moe_route_workspace_bytes.restype = sz
     lib.moe_route.argtypes = [vp, i32, vp, vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.moe_route.restype = i32
@@ -138,8 +138,8 @@ def moe_rows_max(T: int, k: int, E: int, C: int) -> int:
     return int(load_library().moe_rows_max(T, k, E, C))
 
 
-def moe_route_workspace_bytes(T: int, H: int, E: int) -> int:
-    return int(load_library().moe_route_workspace_bytes(T, H, E))
+def moe_route_workspace_bytes(T: int, H: int, E: int, xdt: int) -> int:
+    return int(load_library().moe_route_workspace_bytes(T, H, E, xdt))
 
 
 def moe_dispatch_workspace_bytes(T: int, k: int, E: int) -> int:
@@ -213,7 +213,7 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torc
         else:
             _ptr(logit_bias, "logit_bias", torch.float32, (T, E), dev)
             stride = E
-    ws = _workspace(moe_route_workspace_bytes(T, H, E), workspace, dev)
+    ws = _workspace(moe_route_workspace_bytes(T, H, E, _dtype_code(x)), workspace, dev)
     st = load_library().moe_route(
         _ptr(x, "x", device=dev), _dtype_code(x), _ptr(w_router, "w_router", torch.float32, (E, H), dev),
         _ptr(logit_bias, "logit_bias"), stride, T, H, E, k,

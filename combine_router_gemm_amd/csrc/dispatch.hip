@@ -19,9 +19,9 @@
 //                    pair's rank inside its block (to pair_local).
 //   dispatch_scan    one workgroup: per expert, an exclusive scan of blk_count over blocks (in place),
 //                    count / kept / overflow, then an exclusive scan of kept over experts -> offsets.
-//   dispatch_scatter one wave per token: position = block base + rank in block; kept pairs write the
-//                    layout entries, and the token row is read once and stored to each kept row with
-//                    16-byte vector loads and non-temporal stores.
+//   dispatch_scatter workgroups of 256 threads over (token, 16-byte column slices): position = block
+//                    base + rank in block; kept pairs write the layout entries, and each slice of the
+//                    token row is read once and stored to every kept row (non-temporal stores).
 #include "common.h"
 #include "kernels.h"
 
@@ -116,10 +116,16 @@ __global__ __launch_bounds__(DS_THREADS) void dispatch_scan_kernel(int* __restri
   const int wave = e >> 6;
   int total = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = blk_count[(int64_t)b * E + e];
-      blk_count[(int64_t)b * E + e] = total;  // becomes the block's base position for expert e
-      total += c;
+    // 16 blocks at a time: the loads are independent, so they are all in flight together
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = b0 + i < nblk ? blk_count[(int64_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (b0 + i < nblk) blk_count[(int64_t)(b0 + i) * E + e] = total;  // the block's base for expert e
+        total += c[i];
+      }
     }
   }
   const int kp = e < E ? min(total, C) : 0;
@@ -143,45 +149,66 @@ __global__ __launch_bounds__(DS_THREADS) void dispatch_scan_kernel(int* __restri
   if (e == E - 1) offset[E] = wbase + incl;
 }
 
-template <typename T>
+// grid: T * chunks workgroups of 256 threads. Workgroup (t, c): its first k threads resolve the
+// positions of token t's pairs (chunk 0 also writes the layout entries), then every thread copies VPT
+// 16-byte column slices of x[t] (c*256*VPT + i*256 + tid) to each kept row.
+template <typename T, int VPT>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const T* __restrict__ x, const int* __restrict__ ids,
-                                                              int T_, int H, int k, int E, int C,
+                                                              int H, int k, int E, int C, int chunks,
                                                               const int* __restrict__ blk_base,
                                                               const int* __restrict__ pair_local,
                                                               const int* __restrict__ offset,
                                                               int* __restrict__ row_token, int* __restrict__ row_slot,
                                                               int* __restrict__ pair_row, T* __restrict__ send_buf) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (t >= T_) return;
-  int row = -1;
-  if (lane < k) {
-    const int64_t p = (int64_t)t * k + lane;
+  __shared__ int s_row[MOE_MAX_TOPK];
+  const int t = blockIdx.x / chunks;
+  const int c = blockIdx.x % chunks;
+  const int tid = threadIdx.x;
+  if (tid < k) {
+    const int64_t p = (int64_t)t * k + tid;
     const int e = ids[p];
     const int local = pair_local[p];
+    int row = -1;
     if (e >= 0 && e < E && local >= 0) {
       const int pos = blk_base[(int64_t)(t / DISPATCH_TB) * E + e] + local;
-      if (pos < C) {
-        row = offset[e] + pos;
+      if (pos < C) row = offset[e] + pos;
+    }
+    s_row[tid] = row;
+    if (c == 0) {
+      pair_row[p] = row;
+      if (row >= 0) {
         row_token[row] = t;
-        row_slot[row] = lane;
+        row_slot[row] = tid;
       }
     }
-    pair_row[p] = row;
   }
-  int rows[MOE_MAX_TOPK];
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) rows[j] = __shfl(row, j, 64);
-
+  __syncthreads();
   constexpr int VN = Vec<T>::N;
   const int nvec = H / VN;
-  const T* src = x + (int64_t)t * H;
-  for (int v = lane; v < nvec; v += 64) {
-    const u32x4 val = ld16(src + (int64_t)v * VN);
+  const int v0 = c * 256 * VPT + tid;
+  u32x4 val[VPT];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if (j < k && rows[j] >= 0) st16_nt(send_buf + (int64_t)rows[j] * H + (int64_t)v * VN, val);
+  for (int i = 0; i < VPT; ++i)
+    if (v0 + i * 256 < nvec) val[i] = ld16(x + (int64_t)t * H + (int64_t)(v0 + i * 256) * VN);
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j < k && s_row[j] >= 0) {
+      T* dst = send_buf + (int64_t)s_row[j] * H;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (v0 + i * 256 < nvec) st16_nt(dst + (int64_t)(v0 + i * 256) * VN, val[i]);
+    }
   }
+}
+
+template <typename T, int VPT>
+void launch_scatter_t(const void* x, const int* ids, const moe_layout_t& L, void* send_buf, const int* blk_base,
+                      const int* pair_local, hipStream_t stream) {
+  const int chunks = ceil_div_host(L.H / Vec<T>::N, 256 * VPT);
+  const unsigned blocks = (unsigned)((int64_t)L.T * chunks);
+  dispatch_scatter_kernel<T, VPT><<<blocks, 256, 0, stream>>>(
+      static_cast<const T*>(x), ids, L.H, L.k, L.E, L.C, chunks, blk_base, pair_local, L.expert_offset, L.row_token,
+      L.row_slot, L.pair_row, static_cast<T*>(send_buf));
 }
 
 }  // namespace
@@ -196,15 +223,17 @@ hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const mo
   dispatch_scan_kernel<<<1, DS_THREADS, 0, stream>>>(blk_count, nblk, L.E, L.C, L.expert_count, L.expert_kept,
                                                      L.expert_overflow, L.expert_offset);
   if (L.T == 0) return hipGetLastError();
-  const int blocks = ceil_div_host(L.T, 4);
-  if (xdt_bf16)
-    dispatch_scatter_kernel<bf16_t><<<blocks, 256, 0, stream>>>(
-        static_cast<const bf16_t*>(x), ids, L.T, L.H, L.k, L.E, L.C, blk_count, pair_local, L.expert_offset,
-        L.row_token, L.row_slot, L.pair_row, static_cast<bf16_t*>(send_buf));
-  else
-    dispatch_scatter_kernel<float><<<blocks, 256, 0, stream>>>(
-        static_cast<const float*>(x), ids, L.T, L.H, L.k, L.E, L.C, blk_count, pair_local, L.expert_offset,
-        L.row_token, L.row_slot, L.pair_row, static_cast<float*>(send_buf));
+  const int nvec = L.H / (xdt_bf16 ? 8 : 4);
+  const int vpt = nvec >= 768 ? 4 : (nvec >= 384 ? 2 : 1);
+  if (xdt_bf16) {
+    if (vpt == 4) launch_scatter_t<bf16_t, 4>(x, ids, L, send_buf, blk_count, pair_local, stream);
+    else if (vpt == 2) launch_scatter_t<bf16_t, 2>(x, ids, L, send_buf, blk_count, pair_local, stream);
+    else launch_scatter_t<bf16_t, 1>(x, ids, L, send_buf, blk_count, pair_local, stream);
+  } else {
+    if (vpt == 4) launch_scatter_t<float, 4>(x, ids, L, send_buf, blk_count, pair_local, stream);
+    else if (vpt == 2) launch_scatter_t<float, 2>(x, ids, L, send_buf, blk_count, pair_local, stream);
+    else launch_scatter_t<float, 1>(x, ids, L, send_buf, blk_count, pair_local, stream);
+  }
   return hipGetLastError();
 }
 

@@ -13,7 +13,11 @@ inline int64_t ceil_div_host64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // ---- route ----
-int route_splits(int T, int H, int E, int num_cus);
+struct RouteTiles {
+  int BM, BN;
+};
+RouteTiles route_tiles(int T, int xdt_bf16);
+int route_splits(int T, int H, int E, int xdt_bf16, int num_cus);
 int route_k_split(int H, int splits);
 hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, const float* bias,
                         int64_t bias_stride, int T, int H, int E, int k, float* logits, int* ids, float* wts,

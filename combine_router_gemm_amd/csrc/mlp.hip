@@ -8,10 +8,11 @@
 // sets.
 //
 // Kernels:
-//   mlp_plan      one workgroup. M_l = sum_r kept[r*El + l]; prefix sums give each local expert's
-//                 first row in "plan order" (local expert major, then rank segment, then token) and
-//                 its first M-tile; perm[p] = send-buffer row of plan row p. Everything the GEMMs need
-//                 is derived on the device from the dispatch counts: no host synchronisation.
+//   mlp_plan      M_l = sum_r kept[r*El + l]; prefix sums give each local expert's first row in "plan
+//                 order" (local expert major, then rank segment, then token) and its first M-tile;
+//                 perm[p] = send-buffer row of plan row p. Every workgroup recomputes the small scans
+//                 and fills perm for its own slice of rows. Everything the GEMMs need is derived on the
+//                 device from the dispatch counts: no host synchronisation.
 //   mlp_gemm      persistent MFMA GEMM, C[p, n] = sum_k A[p, k] * B[n, k] ("NT": both operands are
 //                 K-contiguous, the nn.Linear [out, in] layout). Tiles are visited local expert major,
 //                 then N tile, then M tile, so workgroups running side by side share a weight slice;
@@ -35,53 +36,93 @@ namespace {
 // ------------------------------------------------------------------------------------------------
 // plan layout (int32): [0] total M-tiles, [1] total rows, [2 .. 2+El] row start per local expert
 // (El+1 entries), [3+El .. 3+2El] M-tile start per local expert (El+1 entries).
-constexpr int PLAN_THREADS = 1024;
+constexpr int PLAN_THREADS = 1024;  // >= MOE_MAX_EXPERTS: one thread per (local or global) expert
+constexpr int PLAN_ROWS_PER_WG = 4096;
 
 __global__ __launch_bounds__(PLAN_THREADS) void mlp_plan_kernel(const int* __restrict__ kept,
                                                                const int* __restrict__ offset, int E, int El,
                                                                int BM, int* __restrict__ plan,
                                                                int* __restrict__ perm) {
-  __shared__ int s_rows[MOE_MAX_EXPERTS + 1];
-  __shared__ int s_tiles[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_rows[MOE_MAX_EXPERTS + 1];   // per local expert: first plan row (exclusive scan)
+  __shared__ int s_tiles[MOE_MAX_EXPERTS + 1];  // per local expert: first M-tile
+  __shared__ int s_kept[MOE_MAX_EXPERTS];
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_dst[MOE_MAX_EXPERTS];        // per global expert: first plan row
+  __shared__ int s_wsum[2][PLAN_THREADS / MOE_WAVE];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int R = E / El;
-  if (tid < El) {
-    int m = 0;
-    for (int r = 0; r < R; ++r) m += kept[r * El + tid];
-    s_rows[tid] = m;
-    s_tiles[tid] = (m + BM - 1) / BM;
+  if (tid < E) {
+    s_kept[tid] = kept[tid];
+    s_off[tid] = offset[tid];
   }
   __syncthreads();
-  if (tid == 0) {
-    // El <= 512: a serial scan is a few microseconds at most and keeps the plan obviously ordered
-    int acc_r = 0, acc_t = 0;
-    for (int l = 0; l < El; ++l) {
-      const int m = s_rows[l], t = s_tiles[l];
-      s_rows[l] = acc_r;
-      s_tiles[l] = acc_t;
-      acc_r += m;
-      acc_t += t;
+  int m = 0, tl = 0;
+  if (tid < El) {
+    for (int r = 0; r < R; ++r) m += s_kept[r * El + tid];
+    tl = (m + BM - 1) / BM;
+  }
+  // exclusive scan of (rows, tiles) over local experts: wave scans, then wave totals
+  int im = m, it = tl;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int vm = __shfl_up(im, off, 64), vt = __shfl_up(it, off, 64);
+    if (lane >= off) {
+      im += vm;
+      it += vt;
     }
-    s_rows[El] = acc_r;
-    s_tiles[El] = acc_t;
-    plan[0] = acc_t;
-    plan[1] = acc_r;
+  }
+  if (lane == 63) {
+    s_wsum[0][wave] = im;
+    s_wsum[1][wave] = it;
+  }
+  __syncthreads();
+  int bm = 0, bt = 0;
+  for (int w = 0; w < wave; ++w) {
+    bm += s_wsum[0][w];
+    bt += s_wsum[1][w];
+  }
+  if (tid < El) {
+    s_rows[tid] = bm + im - m;
+    s_tiles[tid] = bt + it - tl;
+  }
+  if (tid == El - 1) {
+    s_rows[El] = bm + im;
+    s_tiles[El] = bt + it;
+    if (blockIdx.x == 0) {
+      plan[0] = bt + it;
+      plan[1] = bm + im;
+    }
   }
   __syncthreads();
   int* row_start = plan + 2;
   int* tile_start = plan + 3 + El;
-  for (int l = tid; l <= El; l += PLAN_THREADS) {
-    row_start[l] = s_rows[l];
-    tile_start[l] = s_tiles[l];
+  if (blockIdx.x == 0 && tid <= El) {
+    row_start[tid] = s_rows[tid];
+    tile_start[tid] = s_tiles[tid];
   }
-  // perm: one thread per global expert e copies its kept rows into local expert (e mod El)'s range
-  for (int e = tid; e < E; e += PLAN_THREADS) {
-    const int l = e % El, r = e / El;
+  // global expert e = r*El + l lands after the rows of experts l, El + l, ..., (r-1)*El + l
+  if (tid < E) {
+    const int l = tid % El, r = tid / El;
     int dst = s_rows[l];
-    for (int rr = 0; rr < r; ++rr) dst += kept[rr * El + l];
-    const int src = offset[e];
-    const int n = kept[e];
-    for (int i = 0; i < n; ++i) perm[dst + i] = src + i;
+    for (int rr = 0; rr < r; ++rr) dst += s_kept[rr * El + l];
+    s_dst[tid] = dst;
+  }
+  if (tid == 0) s_off[E] = offset[E];
+  __syncthreads();
+  // perm[p] = send-buffer row of plan row p. Workgroup b handles send-buffer rows
+  // [b * PLAN_ROWS_PER_WG, (b + 1) * PLAN_ROWS_PER_WG): the expert of row q is found by a binary search
+  // over the offsets, and q goes to its expert's plan range.
+  const int total = s_off[E];
+  const int q_end = min(total, (int)((blockIdx.x + 1) * PLAN_ROWS_PER_WG));
+  for (int q = blockIdx.x * PLAN_ROWS_PER_WG + tid; q < q_end; q += PLAN_THREADS) {
+    int lo = 0, hi = E;  // invariant: s_off[lo] <= q < s_off[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_off[mid] <= q) lo = mid;
+      else hi = mid;
+    }
+    perm[s_dst[lo] + (q - s_off[lo])] = q;
   }
 }
 
@@ -322,11 +363,32 @@ void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
   mlp_gemm_kernel<T, BM, BN, BK, WM, WN, GATED><<<grid, WM * WN * 64, 0, stream>>>(a);
 }
 
-// workgroups per CU for the persistent grid
-constexpr int WG_PER_CU = 2;
+// Tile shapes of the few-rows-per-expert (weight streaming) kernels and the persistent grid size in
+// workgroups per CU; overridable at compile time for tuning sweeps.
+#ifndef MOE_DEC_GU_BN
+#define MOE_DEC_GU_BN 128
+#endif
+#ifndef MOE_DEC_GU_BK
+#define MOE_DEC_GU_BK 128
+#endif
+#ifndef MOE_DEC_DN_BN
+#define MOE_DEC_DN_BN 64
+#endif
+#ifndef MOE_DEC_DN_BK
+#define MOE_DEC_DN_BK 256
+#endif
+#ifndef MOE_DEC_WPC
+#define MOE_DEC_WPC 3
+#endif
+#ifndef MOE_PRE_WPC
+#define MOE_PRE_WPC 2
+#endif
 
-int persistent_grid(int64_t max_tiles, int num_cus) {
-  int64_t g = (int64_t)num_cus * WG_PER_CU;
+constexpr int DEC_GU_WN = MOE_DEC_GU_BN / 32 < 4 ? MOE_DEC_GU_BN / 32 : 4;
+constexpr int DEC_DN_WN = MOE_DEC_DN_BN / 16 < 4 ? MOE_DEC_DN_BN / 16 : 4;
+
+int persistent_grid(int64_t max_tiles, int num_cus, int wpc) {
+  int64_t g = (int64_t)num_cus * wpc;
   if (max_tiles < g) g = max_tiles;
   if (g >= 8) g &= ~7ll;  // a multiple of the XCD count keeps the XCD-aware order exact
   return (int)(g > 0 ? g : 1);
@@ -349,9 +411,11 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
                              const MlpTiles& tiles, int num_cus, hipStream_t stream) {
   const int El = L.E / L.R;
   const int H = L.H;
-  mlp_plan_kernel<<<1, PLAN_THREADS, 0, stream>>>(L.expert_kept, L.expert_offset, L.E, El, tiles.BM, plan, perm);
-
   const int64_t rows_max = moe_rows_max(L.T, L.k, L.E, L.C);
+  const int plan_blocks = (int)(rows_max > 0 ? ceil_div_host64(rows_max, PLAN_ROWS_PER_WG) : 1);
+  mlp_plan_kernel<<<plan_blocks, PLAN_THREADS, 0, stream>>>(L.expert_kept, L.expert_offset, L.E, El, tiles.BM, plan,
+                                                            perm);
+
   const int64_t max_mtiles = ceil_div_host64(rows_max, tiles.BM) + El;
 
   GemmArgs gu{};
@@ -386,23 +450,23 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
 
   switch (tiles.variant) {
     case 0: {  // bf16, many rows per expert: 128x128 tiles, 2x2 waves of 64x64
-      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 64), num_cus);
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 64), num_cus, MOE_PRE_WPC);
       launch_gemm<bf16_t, 128, 128, 64, 2, 2, true>(gu, g1, stream);
-      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 128), num_cus);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 128), num_cus, MOE_PRE_WPC);
       launch_gemm<bf16_t, 128, 128, 64, 2, 2, false>(dn, g2, stream);
       break;
     }
     case 1: {  // bf16, few rows per expert: stream the weights with 32-row tiles
-      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 64), num_cus);
-      launch_gemm<bf16_t, 32, 128, 64, 1, 4, true>(gu, g1, stream);
-      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 64), num_cus);
-      launch_gemm<bf16_t, 32, 64, 64, 1, 4, false>(dn, g2, stream);
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_DEC_GU_BN / 2), num_cus, MOE_DEC_WPC);
+      launch_gemm<bf16_t, 32, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true>(gu, g1, stream);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
+      launch_gemm<bf16_t, 32, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false>(dn, g2, stream);
       break;
     }
     default: {  // fp32
-      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus);
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus, 2);
       launch_gemm<float, 32, 64, 32, 1, 2, true>(gu, g1, stream);
-      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 64), num_cus);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 64), num_cus, 2);
       launch_gemm<float, 32, 64, 32, 1, 2, false>(dn, g2, stream);
       break;
     }

@@ -4,9 +4,10 @@
 // weights come from the router's distribution ("Efficient and portable mixture-of-experts
 // communication", section "Introductie").
 //
-// Kernel 1 (route_gemm): split-K fp32 MFMA GEMM. Grid (token tiles, expert tiles, K splits); each
-//   workgroup writes an fp32 partial [T, E] for its K range. x is widened to fp32 exactly (bf16 is the
-//   top half of an fp32 word), so products are the fp32 products of the inputs.
+// Kernel 1 (route_gemm): split-K GEMM. Grid (token tiles, expert tiles, K splits); each workgroup
+//   writes an fp32 partial [T, E] for its K range. fp32 activations run on fp32 MFMA. bf16
+//   activations run on bf16 MFMA with the router weight split exactly into three bf16 parts, so
+//   every product is the exact fp32 product of the inputs and the sum is accumulated in fp32.
 // Kernel 2 (route_topk): sums the K-split partials in a fixed order (deterministic), adds the bias,
 //   (with a single split the partial buffer is the logits buffer itself, read then overwritten in place),
 //   writes the logits and selects the top-k per token with a lane-group arg-max: G lanes per token,
@@ -142,6 +143,116 @@ __global__ __launch_bounds__(256) void route_gemm_kernel(const TX* __restrict__ 
     }
 }
 
+// Exact three-way split of an fp32 weight into bf16 parts, w = hi + mid + lo: hi keeps the top 8
+// significant bits (truncation), mid the next 8 of the exact remainder, lo the last 8 (exact in bf16).
+// With a bf16 activation every product x*hi, x*mid, x*lo is exact in fp32, so three bf16 MFMAs
+// accumulating in fp32 give the fp32 dot product up to accumulation order.
+__device__ __forceinline__ void split3_bf16(float w, uint16_t& h, uint16_t& m, uint16_t& l) {
+  const uint32_t u = __float_as_uint(w);
+  const float fh = __uint_as_float(u & 0xffff0000u);
+  const float r1 = w - fh;  // exact: the bits of w below hi
+  const uint32_t u1 = __float_as_uint(r1);
+  const float fm = __uint_as_float(u1 & 0xffff0000u);
+  const float r2 = r1 - fm;  // exact, at most 8 significant bits
+  h = (uint16_t)(u >> 16);
+  m = (uint16_t)(u1 >> 16);
+  l = __builtin_bit_cast(uint16_t, (bf16_t)r2);
+}
+
+// bf16 activations: BM x BN tiles, 32-deep stages, WM x WN waves of 16x16x32 bf16 MFMAs; the router
+// weight stage is split into its three bf16 planes on the way into LDS.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM* WN * 64) void route_gemm_bf16x3_kernel(const bf16_t* __restrict__ x,
+                                                                       const float* __restrict__ w, int T, int H,
+                                                                       int E, int k_split, float* __restrict__ partial) {
+  constexpr int BK = 32;
+  constexpr int LDR = BK + 8;  // 80-byte LDS rows: b128 fragment reads stay conflict-free
+  constexpr int NTH = WM * WN * 64;
+  constexpr int A_VEC = BM * (BK / 8) / NTH;  // 16-byte bf16 vectors per thread
+  constexpr int B_VEC = BN * (BK / 4) / NTH;  // 16-byte fp32 vectors per thread
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  static_assert(A_VEC >= 1 && B_VEC >= 1 && BM * (BK / 8) % NTH == 0 && BN * (BK / 4) % NTH == 0, "loader");
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[3][BN * LDR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int t0 = blockIdx.x * BM, e0 = blockIdx.y * BN;
+  const int kbeg = blockIdx.z * k_split;
+  const int kend = min(H, kbeg + k_split);
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 ra[A_VEC], rb[B_VEC];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_VEC; ++i) {
+      const int idx = tid + i * NTH, r = idx / (BK / 8), c = (idx % (BK / 8)) * 8;
+      ra[i] = (t0 + r < T && k0 + c < kend) ? ld16(x + (int64_t)(t0 + r) * H + k0 + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < B_VEC; ++i) {
+      const int idx = tid + i * NTH, r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
+      rb[i] = (e0 + r < E && k0 + c < kend) ? ld16(w + (int64_t)(e0 + r) * H + k0 + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < A_VEC; ++i) {
+      const int idx = tid + i * NTH, r = idx / (BK / 8), c = (idx % (BK / 8)) * 8;
+      st16(&As[r * LDR + c], ra[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < B_VEC; ++i) {
+      const int idx = tid + i * NTH, r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
+      uint16_t hv[4], mv[4], lv[4];
+      float f[4];
+      unpack(rb[i], f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split3_bf16(f[q], hv[q], mv[q], lv[q]);
+      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2*>(&Bs[0][r * LDR + c]) = u32x2{hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16)};
+      *reinterpret_cast<u32x2*>(&Bs[1][r * LDR + c]) = u32x2{mv[0] | ((uint32_t)mv[1] << 16), mv[2] | ((uint32_t)mv[3] << 16)};
+      *reinterpret_cast<u32x2*>(&Bs[2][r * LDR + c]) = u32x2{lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16)};
+    }
+    __syncthreads();
+    if (k0 + BK < kend) load(k0 + BK);
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+    u32x4 af[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = ld16(&As[(wm * (BM / WM) + i * 16 + fr) * LDR + fk]);
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const u32x4 bfr = ld16(&Bs[pl][(wn * (BN / WN) + j * 16 + fr) * LDR + fk]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                              __builtin_bit_cast(bf16x8, bfr), acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  float* out = partial + (int64_t)blockIdx.z * T * E;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = e0 + wn * (BN / WN) + j * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = t0 + wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
+        if (row < T && col < E) out[(int64_t)row * E + col] = acc[i][j][r];
+      }
+    }
+}
+
 // (value, id) ordering of the selection: larger value first, then lower id. NaN never wins a
 // comparison, so it is treated as -inf.
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
@@ -164,20 +275,38 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, i
 
   float val[VMAX];
   bool taken[VMAX];
+  float sum[VMAX];
+#pragma unroll
+  for (int i = 0; i < VMAX; ++i) {
+    const int e = i * G + g;
+    taken[i] = !(i < V && e < E && live);
+    sum[i] = taken[i] ? 0.f : partial[(int64_t)t * E + e];
+  }
+  // the remaining K-split partials, four splits of loads in flight at a time, added in split order
+  const int64_t TE = (int64_t)T * E;
+  for (int sp0 = 1; sp0 < splits; sp0 += 4) {
+    float tmp[4][VMAX];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i)
+        tmp[u][i] = (!taken[i] && sp0 + u < splits) ? partial[(sp0 + u) * TE + (int64_t)t * E + i * G + g] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i)
+        if (sp0 + u < splits) sum[i] += tmp[u][i];
+  }
 #pragma unroll
   for (int i = 0; i < VMAX; ++i) {
     val[i] = -INFINITY;
-    taken[i] = true;
-    const int e = i * G + g;
-    if (i < V && e < E && live) {
-      const int64_t idx = (int64_t)t * E + e;
-      float s = partial[idx];
-      for (int sp = 1; sp < splits; ++sp) s += partial[(int64_t)sp * T * E + idx];
+    if (!taken[i]) {
+      const int e = i * G + g;
+      float s = sum[i];
       if (bias) s += bias[(int64_t)t * bias_stride + e];
-      logits[idx] = s;
-      s = s + 0.0f;                     // -0 -> +0: equal values compare equal either way
+      logits[(int64_t)t * E + e] = s;
+      s = s + 0.0f;                       // -0 -> +0: equal values compare equal either way
       val[i] = (s == s) ? s : -INFINITY;  // NaN ranks as -inf
-      taken[i] = false;
     }
   }
 
@@ -239,10 +368,17 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, i
 
 }  // namespace
 
-// Host-side planning of the split-K factor: enough workgroups to cover the chip twice, each split at
-// least 256 K-elements long and a multiple of the 32-wide stage.
-int route_splits(int T, int H, int E, int num_cus) {
-  const int tiles = ceil_div_host(T, RG_BM) * ceil_div_host(E, RG_BN);
+// Host-side planning. Tile shape: fp32 activations use 64x64 fp32-MFMA tiles; bf16 activations use
+// 128x128 bf16x3 tiles for many tokens and 64x64 for few. The split-K factor gives enough workgroups
+// to cover the chip twice, each split at least 256 K-elements long and a multiple of the 32-wide stage.
+RouteTiles route_tiles(int T, int xdt_bf16) {
+  if (xdt_bf16 && T >= 2048) return RouteTiles{128, 128};
+  return RouteTiles{64, 64};
+}
+
+int route_splits(int T, int H, int E, int xdt_bf16, int num_cus) {
+  const RouteTiles rt = route_tiles(T, xdt_bf16);
+  const int tiles = ceil_div_host(T, rt.BM) * ceil_div_host(E, rt.BN);
   int s = ceil_div_host(2 * num_cus, tiles > 0 ? tiles : 1);
   const int smax = H / 256 > 0 ? H / 256 : 1;
   if (s > smax) s = smax;
@@ -260,10 +396,14 @@ hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, cons
                         float* partial, int splits, hipStream_t stream) {
   const int k_split = route_k_split(H, splits);
   const int nsplit = ceil_div_host(H, k_split);
-  dim3 grid(ceil_div_host(T, RG_BM), ceil_div_host(E, RG_BN), nsplit);
-  if (xdt_bf16)
-    route_gemm_kernel<bf16_t><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H, E,
-                                                        k_split, partial);
+  const RouteTiles rt = route_tiles(T, xdt_bf16);
+  dim3 grid(ceil_div_host(T, rt.BM), ceil_div_host(E, rt.BN), nsplit);
+  if (xdt_bf16 && rt.BM == 128)
+    route_gemm_bf16x3_kernel<128, 128, 2, 2><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H,
+                                                                       E, k_split, partial);
+  else if (xdt_bf16)
+    route_gemm_bf16x3_kernel<64, 64, 2, 2><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H, E,
+                                                                     k_split, partial);
   else
     route_gemm_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), w_router, T, H, E, k_split,
                                                        partial);

@@ -61,9 +61,13 @@ def test_workspace_sizes(lib):
     # h [rows_max, F] bf16 dominates the MLP workspace
     assert moe.moe_expert_mlp_workspace_bytes(4096, 8, 256, 8, 128, 2048, moe.MOE_BF16) >= 32768 * 2048 * 2
     assert moe.moe_expert_mlp_workspace_bytes(256, 2, 8, 1, 80, 256, moe.MOE_F32) >= 512 * 256 * 4
-    # the router needs scratch only when the H reduction is split
-    assert moe.moe_route_workspace_bytes(16384, 7168, 256) == 0
-    assert moe.moe_route_workspace_bytes(128, 4096, 8) > 0
+    # the router needs scratch only when the H reduction is split: whole [T, E] fp32 partials
+    for T, H, E in ((16384, 7168, 256), (128, 4096, 8), (256, 128, 8), (4096, 7168, 256)):
+        for xdt in (moe.MOE_BF16, moe.MOE_F32):
+            n = moe.moe_route_workspace_bytes(T, H, E, xdt)
+            assert n % (T * E * 4) == 0 and n != T * E * 4
+    assert moe.moe_route_workspace_bytes(128, 4096, 8, moe.MOE_BF16) > 0
+    assert moe.moe_route_workspace_bytes(128, 4096, 8, 9) == 0
 
 
 def _route(lib, **kw):
