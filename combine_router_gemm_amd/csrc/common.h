@@ -101,4 +101,10 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, then s_barrier.
+// __syncthreads() also fences global memory, which makes every wave wait for all of its global loads
+// in flight (s_waitcnt vmcnt(0)) and so drains a software prefetch pipeline at each barrier. The
+// "memory" clobber keeps the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace moe

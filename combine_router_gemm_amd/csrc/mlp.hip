@@ -21,9 +21,10 @@
 //                 Gate/up pass: A rows gathered through perm from the send buffer, B = the gate and the
 //                 up rows of the same output columns, epilogue h = silu(g) * u (fp32) stored as xdt.
 //                 Down pass: A = h in plan order, epilogue stores to out_buf[perm[p]] as xdt.
-//   Operands are staged through LDS (global -> registers -> LDS, the next stage's global loads in
-//   flight while MFMAs run on the current one). bf16 uses v_mfma_f32_16x16x32_bf16, fp32 uses
-//   v_mfma_f32_16x16x4_f32; both accumulate in fp32.
+//   Operands are staged global -> registers -> LDS with several stages of global loads in flight and
+//   two LDS stages (one barrier per stage). Compute-bound bf16 tiles use v_mfma_f32_32x32x16_bf16,
+//   weight-streaming bf16 tiles v_mfma_f32_16x16x32_bf16, fp32 v_mfma_f32_16x16x4_f32; all accumulate
+//   in fp32.
 #include "common.h"
 #include "kernels.h"
 
@@ -129,24 +130,40 @@ __global__ __launch_bounds__(PLAN_THREADS) void mlp_plan_kernel(const int* __res
 // ------------------------------------------------------------------------------------------------
 // GEMM
 // ------------------------------------------------------------------------------------------------
-template <typename T>
-struct Mfma;
+// MFMA instruction choices. Each op multiplies S x KS by KS x S fragments into an S x S fp32 tile.
+// Lane l supplies 8 consecutive K of fragment row (l % S), starting at K = (l / S) * 8; A and B use
+// the same K assignment, so any K order inside a step gives the same sum.
+//   Op16: v_mfma_f32_16x16x32_bf16  (S = 16, KS = 32; output rows 4*(l/16) + q, q < 4)
+//   Op32: v_mfma_f32_32x32x16_bf16  (S = 32, KS = 16; output rows 8*(q/4) + 4*(l/32) + q%4, q < 16)
+//   OpF32: eight v_mfma_f32_16x16x4_f32 (S = 16, KS = 32); step q takes K = (l/16)*8 + q
+// On MI355X the 32x32x16 bf16 form runs at twice the rate of the 16x16x32 form (measured 2.27 vs
+// 1.2 PFLOP/s with independent chains), so compute-bound tiles use Op32.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// bf16: one v_mfma_f32_16x16x32_bf16 per 32-wide K chunk; lane l supplies 8 consecutive K of row l%16
-template <>
-struct Mfma<bf16_t> {
-  static __device__ __forceinline__ void step(f32x4& acc, const u32x4 (&a)[1], const u32x4 (&b)[1]) {
+struct Op16 {
+  static constexpr int S = 16, KS = 32, VPF = 1, NR = 4;
+  using Acc = f32x4;
+  static __device__ __forceinline__ void step(Acc& acc, const u32x4 (&a)[1], const u32x4 (&b)[1]) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[0]), __builtin_bit_cast(bf16x8, b[0]),
                                                   acc, 0, 0, 0);
   }
-  static constexpr int VPF = 1;  // 16-byte vectors per lane per 32-K fragment
+  static __device__ __forceinline__ int out_row(int lane, int q) { return (lane >> 4) * 4 + q; }
 };
 
-// fp32: eight v_mfma_f32_16x16x4_f32 per 32-wide K chunk; step q takes K = (l/16)*8 + q, the same
-// assignment for A and B, so the eight steps cover the chunk once
-template <>
-struct Mfma<float> {
-  static __device__ __forceinline__ void step(f32x4& acc, const u32x4 (&a)[2], const u32x4 (&b)[2]) {
+struct Op32 {
+  static constexpr int S = 32, KS = 16, VPF = 1, NR = 16;
+  using Acc = f32x16;
+  static __device__ __forceinline__ void step(Acc& acc, const u32x4 (&a)[1], const u32x4 (&b)[1]) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]), __builtin_bit_cast(bf16x8, b[0]),
+                                                  acc, 0, 0, 0);
+  }
+  static __device__ __forceinline__ int out_row(int lane, int q) { return (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3); }
+};
+
+struct OpF32 {
+  static constexpr int S = 16, KS = 32, VPF = 2, NR = 4;
+  using Acc = f32x4;
+  static __device__ __forceinline__ void step(Acc& acc, const u32x4 (&a)[2], const u32x4 (&b)[2]) {
     float fa[8], fb[8];
     unpack(a[0], *reinterpret_cast<float(*)[4]>(&fa[0]));
     unpack(a[1], *reinterpret_cast<float(*)[4]>(&fa[4]));
@@ -155,7 +172,7 @@ struct Mfma<float> {
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[q], fb[q], acc, 0, 0, 0);
   }
-  static constexpr int VPF = 2;
+  static __device__ __forceinline__ int out_row(int lane, int q) { return (lane >> 4) * 4 + q; }
 };
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
@@ -176,9 +193,10 @@ struct GemmArgs {
   int El;
 };
 
-// BM x BN tile, BK-deep LDS stages, WM x WN waves. GATED: the B tile holds BN/2 gate rows then the
-// BN/2 up rows of the same output columns, and each wave owns matching gate and up accumulators.
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool GATED>
+// BM x BN tile, BK-deep LDS stages, WM x WN waves, MFMA op Op. GATED: the B tile holds BN/2 gate rows
+// then the BN/2 up rows of the same output columns, and each wave owns matching gate and up
+// accumulators.
+template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB>
 __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
   constexpr int NTH = WM * WN * 64;
   constexpr int VN = Vec<T>::N;           // elements per 16-byte vector
@@ -188,16 +206,22 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
   constexpr int A_VEC = BM * VPR / NTH;   // A vectors loaded per thread per stage
   constexpr int B_VEC = BN * VPR / NTH;
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-  constexpr int TM = WTM / 16;
-  constexpr int TN = GATED ? (BN / 2 / WN) / 16 : WTN / 16;  // per half when gated
+  constexpr int S = Op::S;
+  constexpr int TM = WTM / S;
+  constexpr int TN = GATED ? (BN / 2 / WN) / S : WTN / S;  // per half when gated
   constexpr int NACC = GATED ? 2 * TN : TN;
   constexpr int OUT_COLS = GATED ? BN / 2 : BN;  // output columns per tile
   static_assert(BM * VPR % NTH == 0 && BN * VPR % NTH == 0, "loader must tile evenly");
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
-  static_assert(BK % 32 == 0, "BK must be a multiple of the 32-wide MFMA chunk");
+  static_assert(BK % Op::KS == 0 && BK % 32 == 0, "BK must be a multiple of the MFMA K step");
+  static_assert(TM * S == WTM && (GATED ? TN * S * WN * 2 == BN : TN * S == WTN), "wave tile must tile by S");
 
-  __shared__ __attribute__((aligned(16))) T As[BM * LDR];
-  __shared__ __attribute__((aligned(16))) T Bs[BN * LDR];
+  // LDB = 2: two LDS stages, the MFMAs read one while the next stage is written into the other (one
+  // barrier per stage). LDB = 1: one LDS stage and two barriers per stage, half the LDS, so more
+  // workgroups fit on a CU; the RS register stages keep the global loads in flight either way.
+  static_assert(LDB == 1 || LDB == 2, "one or two LDS stages");
+  __shared__ __attribute__((aligned(16))) T As[LDB][BM * LDR];
+  __shared__ __attribute__((aligned(16))) T Bs[LDB][BN * LDR];
 
   const T* __restrict__ A = static_cast<const T*>(args.A);
   const T* __restrict__ W = static_cast<const T*>(args.W);
@@ -235,24 +259,26 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
     const int n0 = nt * OUT_COLS;
     const T* Wl = W + (int64_t)l * args.w_stride;
 
-    // per-thread source rows (fixed for the whole K loop)
+    // per-thread source rows (fixed for the whole K loop). Every load is issued unconditionally from a
+    // valid address (rows past the tile end read the tile's first row, columns past K read the last
+    // vector of the row) and masked to zero when it is written to LDS: a load under a branch would
+    // make the compiler wait for every load in flight before the registers are reused.
     const T* a_src[A_VEC];
     int a_lds[A_VEC];
+    bool a_ok[A_VEC];
 #pragma unroll
     for (int i = 0; i < A_VEC; ++i) {
       const int idx = tid + i * NTH;
       const int r = idx / VPR, c = (idx % VPR) * VN;
       a_lds[i] = r * LDR + c;
-      if (r < m_rows) {
-        const int p = p0 + r;
-        const int src_row = args.a_perm ? args.a_perm[p] : p;
-        a_src[i] = A + (int64_t)src_row * args.lda + c;
-      } else {
-        a_src[i] = nullptr;
-      }
+      a_ok[i] = r < m_rows;
+      const int p = p0 + (a_ok[i] ? r : 0);
+      const int src_row = args.a_perm ? args.a_perm[p] : p;
+      a_src[i] = A + (int64_t)src_row * args.lda;
     }
     const T* b_src[B_VEC];
     int b_lds[B_VEC];
+    bool b_ok[B_VEC];
 #pragma unroll
     for (int i = 0; i < B_VEC; ++i) {
       const int idx = tid + i * NTH;
@@ -267,86 +293,113 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
         ncol = n0 + r;
         wrow = ncol;
       }
-      b_src[i] = ncol < args.N ? Wl + (int64_t)wrow * args.K + c : nullptr;
+      b_ok[i] = ncol < args.N;
+      b_src[i] = Wl + (int64_t)(b_ok[i] ? wrow : 0) * args.K;
     }
 
-    f32x4 acc[TM][NACC];
+    typename Op::Acc acc[TM][NACC];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < NACC; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < NACC; ++j)
+#pragma unroll
+        for (int q = 0; q < Op::NR; ++q) acc[i][j][q] = 0.f;
 
-    u32x4 ra[A_VEC], rb[B_VEC];
+    // RS register stages of global loads in flight: stage s + RS is requested before the MFMAs of
+    // stage s run, and stage s + 1 moves from registers to LDS after them (one barrier per stage).
+    const int nk = (args.K + BK - 1) / BK;
+    u32x4 ra[RS][A_VEC], rb[RS][B_VEC];
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    auto load_stage = [&](int k0) {
+    auto load_stage = [&](int st, u32x4 (&xa)[A_VEC], u32x4 (&xb)[B_VEC]) {
+      const int k0 = st * BK;
 #pragma unroll
-      for (int i = 0; i < A_VEC; ++i) {
-        const int kc = k0 + (a_lds[i] % LDR);
-        ra[i] = (a_src[i] && kc < args.K) ? ld16(a_src[i] + k0) : zero;
-      }
+      for (int i = 0; i < A_VEC; ++i) xa[i] = ld16(a_src[i] + min(k0 + a_lds[i] % LDR, args.K - VN));
 #pragma unroll
-      for (int i = 0; i < B_VEC; ++i) {
-        const int kc = k0 + (b_lds[i] % LDR);
-        rb[i] = (b_src[i] && kc < args.K) ? ld16(b_src[i] + k0) : zero;
-      }
+      for (int i = 0; i < B_VEC; ++i) xb[i] = ld16(b_src[i] + min(k0 + b_lds[i] % LDR, args.K - VN));
     };
-
-    load_stage(0);
-    for (int k0 = 0; k0 < args.K; k0 += BK) {
-      __syncthreads();  // the previous stage's MFMA reads of LDS are done
+    auto store_stage = [&](int st, int buf, const u32x4 (&xa)[A_VEC], const u32x4 (&xb)[B_VEC]) {
+      const int k0 = st * BK;
 #pragma unroll
-      for (int i = 0; i < A_VEC; ++i) st16(&As[a_lds[i]], ra[i]);
+      for (int i = 0; i < A_VEC; ++i) st16(&As[buf][a_lds[i]], (a_ok[i] && k0 + a_lds[i] % LDR < args.K) ? xa[i] : zero);
 #pragma unroll
-      for (int i = 0; i < B_VEC; ++i) st16(&Bs[b_lds[i]], rb[i]);
-      __syncthreads();
-      if (k0 + BK < args.K) load_stage(k0 + BK);
-
-      const int fr = lane & 15;
-      const int fk = (lane >> 4) * 8;  // 8 consecutive K per lane inside each 32-wide chunk
+      for (int i = 0; i < B_VEC; ++i) st16(&Bs[buf][b_lds[i]], (b_ok[i] && k0 + b_lds[i] % LDR < args.K) ? xb[i] : zero);
+    };
+    const int fr = lane % S;
+    const int fk = (lane / S) * 8;  // 8 consecutive K per lane inside each K step
+    auto compute = [&](int buf) {
 #pragma unroll
-      for (int kk = 0; kk < BK; kk += 32) {
-        u32x4 af[TM][Mfma<T>::VPF];
-        u32x4 bfg[NACC][Mfma<T>::VPF];
+      for (int kk = 0; kk < BK; kk += Op::KS) {
+        u32x4 af[TM][Op::VPF];
+        u32x4 bfg[NACC][Op::VPF];
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const T* pa = &As[(wm * WTM + i * 16 + fr) * LDR + kk + fk];
+          const T* pa = &As[buf][(wm * WTM + i * S + fr) * LDR + kk + fk];
 #pragma unroll
-          for (int q = 0; q < Mfma<T>::VPF; ++q) af[i][q] = ld16(pa + q * VN);
+          for (int q = 0; q < Op::VPF; ++q) af[i][q] = ld16(pa + q * VN);
         }
 #pragma unroll
         for (int j = 0; j < NACC; ++j) {
           int brow;
           if (GATED) {
             const int half = j / TN, jj = j % TN;
-            brow = half * (BN / 2) + wn * (BN / 2 / WN) + jj * 16 + fr;
+            brow = half * (BN / 2) + wn * (BN / 2 / WN) + jj * S + fr;
           } else {
-            brow = wn * WTN + j * 16 + fr;
+            brow = wn * WTN + j * S + fr;
           }
-          const T* pb = &Bs[brow * LDR + kk + fk];
+          const T* pb = &Bs[buf][brow * LDR + kk + fk];
 #pragma unroll
-          for (int q = 0; q < Mfma<T>::VPF; ++q) bfg[j][q] = ld16(pb + q * VN);
+          for (int q = 0; q < Op::VPF; ++q) bfg[j][q] = ld16(pb + q * VN);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < NACC; ++j) Mfma<T>::step(acc[i][j], af[i], bfg[j]);
+          for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[i], bfg[j]);
+      }
+    };
+
+    // stages past the last one re-read the last stage (an L2 hit) so that no load sits under a branch
+#pragma unroll
+    for (int u = 0; u < RS; ++u) load_stage(min(u, nk - 1), ra[u], rb[u]);
+    if (LDB == 2) {
+      store_stage(0, 0, ra[0], rb[0]);
+      lds_barrier();
+    }
+    for (int s0 = 0; s0 < nk; s0 += RS) {
+#pragma unroll
+      for (int u = 0; u < RS; ++u) {
+        const int st = s0 + u;  // register slot u holds stage st
+        if (st < nk) {
+          if (LDB == 2) {  // stage st is already in LDS
+            load_stage(min(st + RS, nk - 1), ra[u], rb[u]);
+            compute(st & 1);
+            if (st + 1 < nk) store_stage(st + 1, (st + 1) & 1, ra[(u + 1) % RS], rb[(u + 1) % RS]);
+            lds_barrier();
+          } else {
+            lds_barrier();  // every wave is done reading the previous stage
+            store_stage(st, 0, ra[u], rb[u]);
+            lds_barrier();
+            load_stage(min(st + RS, nk - 1), ra[u], rb[u]);
+            compute(0);
+          }
+        }
       }
     }
+    if (LDB == 1) lds_barrier();  // the next tile overwrites the LDS stage
 
-    // epilogue: lane l holds column l%16 and rows 4*(l/16) + r of each 16x16 accumulator
+    // epilogue: lane l holds column l % S of each S x S accumulator; Op::out_row gives the rows
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const int cl = GATED ? wn * (BN / 2 / WN) + j * 16 + (lane & 15) : wn * WTN + j * 16 + (lane & 15);
+        const int cl = GATED ? wn * (BN / 2 / WN) + j * S + (lane % S) : wn * WTN + j * S + (lane % S);
         const int col = n0 + cl;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wm * WTM + i * 16 + (lane >> 4) * 4 + r;
+        for (int q = 0; q < Op::NR; ++q) {
+          const int row = wm * WTM + i * S + Op::out_row(lane, q);
           if (row < m_rows && col < args.N) {
             float v;
-            if (GATED) v = silu_f32(acc[i][j][r]) * acc[i][j + TN][r];
-            else v = acc[i][j][r];
+            if (GATED) v = silu_f32(acc[i][j][q]) * acc[i][j + TN][q];
+            else v = acc[i][j][q];
             const int p = p0 + row;
             const int orow = args.out_perm ? args.out_perm[p] : p;
             Out[(int64_t)orow * args.ldo + col] = from_f32<T>(v);
@@ -354,38 +407,72 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
         }
       }
     }
-    __syncthreads();  // LDS is reused by the next tile
   }
 }
 
-template <typename T, int BM, int BN, int BK, int WM, int WN, bool GATED>
+template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB>
 void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
-  mlp_gemm_kernel<T, BM, BN, BK, WM, WN, GATED><<<grid, WM * WN * 64, 0, stream>>>(a);
+  mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB><<<grid, WM * WN * 64, 0, stream>>>(a);
 }
 
-// Tile shapes of the few-rows-per-expert (weight streaming) kernels and the persistent grid size in
-// workgroups per CU; overridable at compile time for tuning sweeps.
+// Persistent grid sizes in workgroups per CU and the compute-bound tile shapes; overridable at compile
+// time for tuning sweeps.
+#ifndef MOE_DEC_WPC
+#define MOE_DEC_WPC 3
+#endif
+#ifndef MOE_PRE_WPC
+#define MOE_PRE_WPC 1
+#endif
+// many-rows-per-expert (compute-bound) tiles: BM x BN x BK with WM x WN waves
+#ifndef MOE_PRE_BM
+#define MOE_PRE_BM 128
+#endif
+#ifndef MOE_PRE_BN
+#define MOE_PRE_BN 256
+#endif
+#ifndef MOE_PRE_BK
+#define MOE_PRE_BK 64
+#endif
+#ifndef MOE_PRE_WM
+#define MOE_PRE_WM 2
+#endif
+#ifndef MOE_PRE_WN
+#define MOE_PRE_WN 4
+#endif
+
+#ifndef MOE_PRE_OP
+#define MOE_PRE_OP Op32
+#endif
+// register stages of global prefetch in flight
+#ifndef MOE_PRE_RS
+#define MOE_PRE_RS 2
+#endif
+#ifndef MOE_DEC_RS
+#define MOE_DEC_RS 2
+#endif
+#ifndef MOE_PRE_LDB
+#define MOE_PRE_LDB 2
+#endif
+#ifndef MOE_DEC_LDB
+#define MOE_DEC_LDB 1
+#endif
+// few-rows-per-expert (weight streaming) tiles: 32 rows, BN weight rows, BK deep
 #ifndef MOE_DEC_GU_BN
 #define MOE_DEC_GU_BN 128
 #endif
 #ifndef MOE_DEC_GU_BK
-#define MOE_DEC_GU_BK 128
+#define MOE_DEC_GU_BK 64
 #endif
 #ifndef MOE_DEC_DN_BN
 #define MOE_DEC_DN_BN 64
 #endif
 #ifndef MOE_DEC_DN_BK
-#define MOE_DEC_DN_BK 256
+#define MOE_DEC_DN_BK 128
 #endif
-#ifndef MOE_DEC_WPC
-#define MOE_DEC_WPC 3
-#endif
-#ifndef MOE_PRE_WPC
-#define MOE_PRE_WPC 2
-#endif
-
 constexpr int DEC_GU_WN = MOE_DEC_GU_BN / 32 < 4 ? MOE_DEC_GU_BN / 32 : 4;
 constexpr int DEC_DN_WN = MOE_DEC_DN_BN / 16 < 4 ? MOE_DEC_DN_BN / 16 : 4;
+using PreOp = MOE_PRE_OP;
+
 
 int persistent_grid(int64_t max_tiles, int num_cus, int wpc) {
   int64_t g = (int64_t)num_cus * wpc;
@@ -402,7 +489,7 @@ size_t mlp_plan_ints(int El) { return 2 + 2 * (size_t)(El + 1); }
 MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int xdt_bf16) {
   if (!xdt_bf16) return MlpTiles{32, 2};
   const int64_t per_expert = El > 0 ? rows_max / El : rows_max;
-  if (per_expert >= 128) return MlpTiles{128, 0};
+  if (per_expert >= 128) return MlpTiles{MOE_PRE_BM, 0};
   return MlpTiles{32, 1};
 }
 
@@ -449,25 +536,27 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   dn.El = El;
 
   switch (tiles.variant) {
-    case 0: {  // bf16, many rows per expert: 128x128 tiles, 2x2 waves of 64x64
-      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 64), num_cus, MOE_PRE_WPC);
-      launch_gemm<bf16_t, 128, 128, 64, 2, 2, true>(gu, g1, stream);
-      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 128), num_cus, MOE_PRE_WPC);
-      launch_gemm<bf16_t, 128, 128, 64, 2, 2, false>(dn, g2, stream);
+    case 0: {  // bf16, many rows per expert
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_PRE_BN / 2), num_cus, MOE_PRE_WPC);
+      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB>(gu, g1, stream);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_PRE_BN), num_cus, MOE_PRE_WPC);
+      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, false, MOE_PRE_RS, MOE_PRE_LDB>(dn, g2, stream);
       break;
     }
-    case 1: {  // bf16, few rows per expert: stream the weights with 32-row tiles
+    case 1: {  // bf16, few rows per expert: stream the weights through 32-row tiles
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_DEC_GU_BN / 2), num_cus, MOE_DEC_WPC);
-      launch_gemm<bf16_t, 32, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true>(gu, g1, stream);
+      launch_gemm<bf16_t, Op16, 32, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB>(
+          gu, g1, stream);
       const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
-      launch_gemm<bf16_t, 32, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false>(dn, g2, stream);
+      launch_gemm<bf16_t, Op16, 32, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB>(
+          dn, g2, stream);
       break;
     }
     default: {  // fp32
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus, 2);
-      launch_gemm<float, 32, 64, 32, 1, 2, true>(gu, g1, stream);
+      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, true, 2, 2>(gu, g1, stream);
       const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 64), num_cus, 2);
-      launch_gemm<float, 32, 64, 32, 1, 2, false>(dn, g2, stream);
+      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, false, 2, 2>(dn, g2, stream);
       break;
     }
   }
