@@ -183,6 +183,10 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(const T* __restri
     }
   }
   __syncthreads();
+  bool any = false;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) any |= (j < k && s_row[j] >= 0);
+  if (!any) return;  // every pair of this token was dropped: nothing to copy
   constexpr int VN = Vec<T>::N;
   const int nvec = H / VN;
   const int v0 = c * 256 * VPT + tid;

@@ -27,6 +27,7 @@
 //   in fp32.
 #include "common.h"
 #include "kernels.h"
+#include "mfma.h"
 
 namespace moe {
 
@@ -130,51 +131,6 @@ __global__ __launch_bounds__(PLAN_THREADS) void mlp_plan_kernel(const int* __res
 // ------------------------------------------------------------------------------------------------
 // GEMM
 // ------------------------------------------------------------------------------------------------
-// MFMA instruction choices. Each op multiplies S x KS by KS x S fragments into an S x S fp32 tile.
-// Lane l supplies 8 consecutive K of fragment row (l % S), starting at K = (l / S) * 8; A and B use
-// the same K assignment, so any K order inside a step gives the same sum.
-//   Op16: v_mfma_f32_16x16x32_bf16  (S = 16, KS = 32; output rows 4*(l/16) + q, q < 4)
-//   Op32: v_mfma_f32_32x32x16_bf16  (S = 32, KS = 16; output rows 8*(q/4) + 4*(l/32) + q%4, q < 16)
-//   OpF32: eight v_mfma_f32_16x16x4_f32 (S = 16, KS = 32); step q takes K = (l/16)*8 + q
-// On MI355X the 32x32x16 bf16 form runs at twice the rate of the 16x16x32 form (measured 2.27 vs
-// 1.2 PFLOP/s with independent chains), so compute-bound tiles use Op32.
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-struct Op16 {
-  static constexpr int S = 16, KS = 32, VPF = 1, NR = 4;
-  using Acc = f32x4;
-  static __device__ __forceinline__ void step(Acc& acc, const u32x4 (&a)[1], const u32x4 (&b)[1]) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[0]), __builtin_bit_cast(bf16x8, b[0]),
-                                                  acc, 0, 0, 0);
-  }
-  static __device__ __forceinline__ int out_row(int lane, int q) { return (lane >> 4) * 4 + q; }
-};
-
-struct Op32 {
-  static constexpr int S = 32, KS = 16, VPF = 1, NR = 16;
-  using Acc = f32x16;
-  static __device__ __forceinline__ void step(Acc& acc, const u32x4 (&a)[1], const u32x4 (&b)[1]) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]), __builtin_bit_cast(bf16x8, b[0]),
-                                                  acc, 0, 0, 0);
-  }
-  static __device__ __forceinline__ int out_row(int lane, int q) { return (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3); }
-};
-
-struct OpF32 {
-  static constexpr int S = 16, KS = 32, VPF = 2, NR = 4;
-  using Acc = f32x4;
-  static __device__ __forceinline__ void step(Acc& acc, const u32x4 (&a)[2], const u32x4 (&b)[2]) {
-    float fa[8], fb[8];
-    unpack(a[0], *reinterpret_cast<float(*)[4]>(&fa[0]));
-    unpack(a[1], *reinterpret_cast<float(*)[4]>(&fa[4]));
-    unpack(b[0], *reinterpret_cast<float(*)[4]>(&fb[0]));
-    unpack(b[1], *reinterpret_cast<float(*)[4]>(&fb[4]));
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[q], fb[q], acc, 0, 0, 0);
-  }
-  static __device__ __forceinline__ int out_row(int lane, int q) { return (lane >> 4) * 4 + q; }
-};
-
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 struct GemmArgs {
@@ -196,7 +152,7 @@ struct GemmArgs {
 // BM x BN tile, BK-deep LDS stages, WM x WN waves, MFMA op Op. GATED: the B tile holds BN/2 gate rows
 // then the BN/2 up rows of the same output columns, and each wave owns matching gate and up
 // accumulators.
-template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB>
+template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT>
 __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
   constexpr int NTH = WM * WN * 64;
   constexpr int VN = Vec<T>::N;           // elements per 16-byte vector
@@ -315,7 +271,12 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int i = 0; i < A_VEC; ++i) xa[i] = ld16(a_src[i] + min(k0 + a_lds[i] % LDR, args.K - VN));
 #pragma unroll
-      for (int i = 0; i < B_VEC; ++i) xb[i] = ld16(b_src[i] + min(k0 + b_lds[i] % LDR, args.K - VN));
+      for (int i = 0; i < B_VEC; ++i) {
+        // weights are read once per tile: streaming (non-temporal) loads keep the reused activation
+        // rows resident in L2 when many tiles share them
+        const T* pb = b_src[i] + min(k0 + b_lds[i] % LDR, args.K - VN);
+        xb[i] = BNT ? ld16_nt(pb) : ld16(pb);
+      }
     };
     auto store_stage = [&](int st, int buf, const u32x4 (&xa)[A_VEC], const u32x4 (&xb)[B_VEC]) {
       const int k0 = st * BK;
@@ -410,9 +371,9 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
   }
 }
 
-template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB>
+template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT>
 void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
-  mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB><<<grid, WM * WN * 64, 0, stream>>>(a);
+  mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT><<<grid, WM * WN * 64, 0, stream>>>(a);
 }
 
 // Persistent grid sizes in workgroups per CU and the compute-bound tile shapes; overridable at compile
@@ -538,25 +499,31 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   switch (tiles.variant) {
     case 0: {  // bf16, many rows per expert
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_PRE_BN / 2), num_cus, MOE_PRE_WPC);
-      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB>(gu, g1, stream);
+      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB, false>(gu, g1, stream);
       const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_PRE_BN), num_cus, MOE_PRE_WPC);
-      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, false, MOE_PRE_RS, MOE_PRE_LDB>(dn, g2, stream);
+      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, false, MOE_PRE_RS, MOE_PRE_LDB, false>(dn, g2, stream);
       break;
     }
     case 1: {  // bf16, few rows per expert: stream the weights through 32-row tiles
+      // with many local experts of few rows each, streaming (non-temporal) weight loads in the gate/up
+      // pass measured faster; with few experts the default cache policy did
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_DEC_GU_BN / 2), num_cus, MOE_DEC_WPC);
-      launch_gemm<bf16_t, Op16, 32, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB>(
-          gu, g1, stream);
+      if (El >= 16)
+        launch_gemm<bf16_t, Op16, 32, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true>(
+            gu, g1, stream);
+      else
+        launch_gemm<bf16_t, Op16, 32, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, false>(
+            gu, g1, stream);
       const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
-      launch_gemm<bf16_t, Op16, 32, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB>(
+      launch_gemm<bf16_t, Op16, 32, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB, false>(
           dn, g2, stream);
       break;
     }
     default: {  // fp32
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus, 2);
-      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, true, 2, 2>(gu, g1, stream);
+      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, true, 2, 2, false>(gu, g1, stream);
       const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 64), num_cus, 2);
-      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, false, 2, 2>(dn, g2, stream);
+      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, false, 2, 2, false>(dn, g2, stream);
       break;
     }
   }

@@ -14,6 +14,7 @@
 //   each holding E/G logits, k rounds of a butterfly max over (value desc, expert id asc).
 #include "common.h"
 #include "kernels.h"
+#include "mfma.h"
 
 namespace moe {
 
@@ -159,9 +160,9 @@ __device__ __forceinline__ void split3_bf16(float w, uint16_t& h, uint16_t& m, u
   l = __builtin_bit_cast(uint16_t, (bf16_t)r2);
 }
 
-// bf16 activations: BM x BN tiles, 32-deep stages, WM x WN waves of 16x16x32 bf16 MFMAs; the router
-// weight stage is split into its three bf16 planes on the way into LDS.
-template <int BM, int BN, int WM, int WN>
+// bf16 activations: BM x BN tiles, 32-deep stages, WM x WN waves of Op MFMAs (32x32x16 bf16 by
+// default); the router weight stage is split into its three bf16 planes on the way into LDS.
+template <typename Op, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM* WN * 64) void route_gemm_bf16x3_kernel(const bf16_t* __restrict__ x,
                                                                        const float* __restrict__ w, int T, int H,
                                                                        int E, int k_split, float* __restrict__ partial) {
@@ -170,7 +171,9 @@ __global__ __launch_bounds__(WM* WN * 64) void route_gemm_bf16x3_kernel(const bf
   constexpr int NTH = WM * WN * 64;
   constexpr int A_VEC = BM * (BK / 8) / NTH;  // 16-byte bf16 vectors per thread
   constexpr int B_VEC = BN * (BK / 4) / NTH;  // 16-byte fp32 vectors per thread
-  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int S = Op::S;
+  constexpr int TM = BM / WM / S, TN = BN / WN / S;
+  static_assert(TM * S * WM == BM && TN * S * WN == BN, "wave tile must tile by the MFMA size");
   static_assert(A_VEC >= 1 && B_VEC >= 1 && BM * (BK / 8) % NTH == 0 && BN * (BK / 4) % NTH == 0, "loader");
   __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDR];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[3][BN * LDR];
@@ -181,39 +184,44 @@ __global__ __launch_bounds__(WM* WN * 64) void route_gemm_bf16x3_kernel(const bf
   const int kbeg = blockIdx.z * k_split;
   const int kend = min(H, kbeg + k_split);
 
-  f32x4 acc[TM][TN];
+  typename Op::Acc acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < Op::NR; ++q) acc[i][j][q] = 0.f;
 
+  // loads are unconditional from clamped, valid addresses and masked when written to LDS, so the
+  // compiler can keep the next stage's loads in flight across the barriers
   u32x4 ra[A_VEC], rb[B_VEC];
   auto load = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < A_VEC; ++i) {
       const int idx = tid + i * NTH, r = idx / (BK / 8), c = (idx % (BK / 8)) * 8;
-      ra[i] = (t0 + r < T && k0 + c < kend) ? ld16(x + (int64_t)(t0 + r) * H + k0 + c) : u32x4{0u, 0u, 0u, 0u};
+      ra[i] = ld16(x + (int64_t)min(t0 + r, T - 1) * H + min(k0 + c, kend - 8));
     }
 #pragma unroll
     for (int i = 0; i < B_VEC; ++i) {
       const int idx = tid + i * NTH, r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
-      rb[i] = (e0 + r < E && k0 + c < kend) ? ld16(w + (int64_t)(e0 + r) * H + k0 + c) : u32x4{0u, 0u, 0u, 0u};
+      rb[i] = ld16(w + (int64_t)min(e0 + r, E - 1) * H + min(k0 + c, kend - 4));
     }
   };
+  const u32x4 zero = {0u, 0u, 0u, 0u};
   load(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += BK) {
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < A_VEC; ++i) {
       const int idx = tid + i * NTH, r = idx / (BK / 8), c = (idx % (BK / 8)) * 8;
-      st16(&As[r * LDR + c], ra[i]);
+      st16(&As[r * LDR + c], (t0 + r < T && k0 + c < kend) ? ra[i] : zero);
     }
 #pragma unroll
     for (int i = 0; i < B_VEC; ++i) {
       const int idx = tid + i * NTH, r = idx / (BK / 4), c = (idx % (BK / 4)) * 4;
       uint16_t hv[4], mv[4], lv[4];
       float f[4];
-      unpack(rb[i], f);
+      unpack((e0 + r < E && k0 + c < kend) ? rb[i] : zero, f);
 #pragma unroll
       for (int q = 0; q < 4; ++q) split3_bf16(f[q], hv[q], mv[q], lv[q]);
       typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -221,21 +229,23 @@ __global__ __launch_bounds__(WM* WN * 64) void route_gemm_bf16x3_kernel(const bf
       *reinterpret_cast<u32x2*>(&Bs[1][r * LDR + c]) = u32x2{mv[0] | ((uint32_t)mv[1] << 16), mv[2] | ((uint32_t)mv[3] << 16)};
       *reinterpret_cast<u32x2*>(&Bs[2][r * LDR + c]) = u32x2{lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16)};
     }
-    __syncthreads();
-    if (k0 + BK < kend) load(k0 + BK);
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
-    u32x4 af[TM];
+    lds_barrier();
+    load(k0 + BK);  // past the end the addresses clamp to valid data that is never stored
+    const int fr = lane % S, fk = (lane / S) * 8;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = ld16(&As[(wm * (BM / WM) + i * 16 + fr) * LDR + fk]);
+    for (int kk = 0; kk < BK; kk += Op::KS) {
+      u32x4 af[TM][1];
 #pragma unroll
-    for (int pl = 0; pl < 3; ++pl) {
+      for (int i = 0; i < TM; ++i) af[i][0] = ld16(&As[(wm * (BM / WM) + i * S + fr) * LDR + kk + fk]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const u32x4 bfr = ld16(&Bs[pl][(wn * (BN / WN) + j * 16 + fr) * LDR + fk]);
+      for (int pl = 0; pl < 3; ++pl) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
-                                                              __builtin_bit_cast(bf16x8, bfr), acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) {
+          u32x4 bfr[1];
+          bfr[0] = ld16(&Bs[pl][(wn * (BN / WN) + j * S + fr) * LDR + kk + fk]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i) Op::step(acc[i][j], af[i], bfr);
+        }
       }
     }
   }
@@ -244,11 +254,11 @@ __global__ __launch_bounds__(WM* WN * 64) void route_gemm_bf16x3_kernel(const bf
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = e0 + wn * (BN / WN) + j * 16 + (lane & 15);
+      const int col = e0 + wn * (BN / WN) + j * S + (lane % S);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = t0 + wm * (BM / WM) + i * 16 + (lane >> 4) * 4 + r;
-        if (row < T && col < E) out[(int64_t)row * E + col] = acc[i][j][r];
+      for (int q = 0; q < Op::NR; ++q) {
+        const int row = t0 + wm * (BM / WM) + i * S + Op::out_row(lane, q);
+        if (row < T && col < E) out[(int64_t)row * E + col] = acc[i][j][q];
       }
     }
 }
@@ -399,10 +409,10 @@ hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, cons
   const RouteTiles rt = route_tiles(T, xdt_bf16);
   dim3 grid(ceil_div_host(T, rt.BM), ceil_div_host(E, rt.BN), nsplit);
   if (xdt_bf16 && rt.BM == 128)
-    route_gemm_bf16x3_kernel<128, 128, 2, 2><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H,
+    route_gemm_bf16x3_kernel<Op32, 128, 128, 2, 2><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H,
                                                                        E, k_split, partial);
   else if (xdt_bf16)
-    route_gemm_bf16x3_kernel<64, 64, 2, 2><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H, E,
+    route_gemm_bf16x3_kernel<Op32, 64, 64, 2, 2><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H, E,
                                                                      k_split, partial);
   else
     route_gemm_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), w_router, T, H, E, k_split,
