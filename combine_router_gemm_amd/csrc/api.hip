@@ -144,7 +144,7 @@ int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* la
   int* perm = reinterpret_cast<int*>(ws);
   ws += moe::align256((size_t)rows * sizeof(int));
   void* hbuf = ws;
-  const moe::MlpTiles tiles = moe::mlp_pick_tiles(rows, El, xdt == MOE_BF16);
+  const moe::MlpTiles tiles = moe::mlp_pick_tiles(rows, El, L.H, F, xdt == MOE_BF16);
   return hip_status(moe::launch_expert_mlp(send_buf, xdt == MOE_BF16, L, w_gate_up, w_down, F, out_buf, plan, perm,
                                            hbuf, tiles, device_cus(), stream));
 }

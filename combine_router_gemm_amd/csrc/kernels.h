@@ -34,7 +34,7 @@ struct MlpTiles {
   int BM;       // rows per tile (shared by both GEMMs; the plan is built for it)
   int variant;  // kernel family, see mlp.hip
 };
-MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int xdt_bf16);
+MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16);
 size_t mlp_plan_ints(int El);
 hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
                              const void* w_down, int F, void* out_buf, int* plan, int* perm, void* hbuf,

@@ -193,12 +193,19 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous run of tile ids
+  // XCD-aware order: workgroup b runs on XCD b % 8. The tile list is cut into 8 near-equal contiguous
+  // ranges, one per XCD (neighbouring tiles share operands in that XCD's L2), and the XCD's
+  // workgroups stride through its range, so every XCD gets the same share of the work.
   const int G = gridDim.x;
-  int vb = blockIdx.x;
-  if ((G & 7) == 0) vb = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  int t_begin = blockIdx.x, t_end = total, t_step = G;
+  if ((G & 7) == 0 && G >= 8) {
+    const int x = blockIdx.x & 7, per = (total + 7) >> 3;
+    t_begin = x * per + (blockIdx.x >> 3);
+    t_end = min(total, (x + 1) * per);
+    t_step = G >> 3;
+  }
 
-  for (int tile = vb; tile < total; tile += G) {
+  for (int tile = t_begin; tile < t_end; tile += t_step) {
     // tile -> (local expert l, n tile, m tile): l is the last expert with tile_start[l]*n_tiles <= tile
     int lo = 0, hi = El;  // invariant: tile_start[lo]*n_tiles <= tile < tile_start[hi]*n_tiles
     while (hi - lo > 1) {
@@ -371,6 +378,240 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Compute-bound bf16 GEMM with direct global -> LDS loads (buffer_load_dwordx4 ... lds)
+// ------------------------------------------------------------------------------------------------
+// The operands never pass through registers on their way to LDS, so NS stages of loads can be in
+// flight at once without register cost, leaving the register file to the accumulators. One wave load
+// instruction writes 1 KB of LDS: 8 rows of a 64-deep (128-byte) stage. Rows are stored unpadded and
+// the 16-byte chunks of row r are XOR-swizzled (chunk c at position c ^ swz(r)) by choosing which
+// global chunk each lane fetches, so the 32-row MFMA fragment reads hit distinct LDS banks. Rows past
+// the tile are fetched at an offset beyond the buffer's record count, which the hardware returns as
+// zeros. Requires K % 64 == 0 and operand buffers below 2 GiB (the host falls back otherwise).
+// chunk swizzle of row r for CPR 16-byte chunks per row (CPR = 8 for 128-byte rows, 4 for 64-byte rows);
+// SWZ 1 spreads 16 consecutive rows over distinct (row parity, chunk) bank slots
+template <int SWZ, int CPR>
+__device__ __forceinline__ int dl_swz(int r) {
+  if (CPR == 8) return SWZ == 0 ? (r & 7) : ((r >> 1) & 7);
+  return SWZ == 0 ? (r & 3) : ((r >> 2) & 3);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM, int BN, int BK, int WM, int WN, bool GATED, int NS, int SWZ>
+__global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args, int a_bytes) {
+  using Op = Op32;
+  static_assert(BK == 32 || BK == 64, "32- or 64-deep stages");
+  constexpr int S = 32, ROWB = BK * 2;
+  constexpr int CPR = BK / 8;            // 16-byte chunks per LDS row
+  constexpr int RPI = 64 / CPR;          // rows per 1 KB wave load
+  constexpr int NW = WM * WN;
+  constexpr int A_INS = BM / RPI, B_INS = BN / RPI;  // 1 KB wave loads per stage
+  static_assert((A_INS + B_INS) % NW == 0, "wave loads must split evenly");
+  constexpr int LPW = (A_INS + B_INS) / NW;
+  constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int WTM = BM / WM, TM = WTM / S;
+  constexpr int TN = GATED ? (BN / 2 / WN) / S : (BN / WN) / S;
+  constexpr int NACC = GATED ? 2 * TN : TN;
+  constexpr int OUT_COLS = GATED ? BN / 2 : BN;
+  static_assert(NS >= 2 && NS <= 6, "2..6 LDS stages");
+  static_assert(TM >= 1 && TN >= 1, "wave tile too small");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE];
+
+  const bf16_t* A = static_cast<const bf16_t*>(args.A);
+  const bf16_t* W = static_cast<const bf16_t*>(args.W);
+  bf16_t* __restrict__ Out = static_cast<bf16_t*>(args.Out);
+  const int El = args.El;
+  const int* row_start = args.plan + 2;
+  const int* tile_start = args.plan + 3 + El;
+  const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
+  const int total = args.plan[0] * n_tiles;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across the wave: keeping it scalar keeps the buffer descriptor and the
+  // LDS destination of every load in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int nk = args.K / BK;
+  const int OOB = 0x7ffffff0;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, a_bytes, 0x00020000);
+  const int w_bytes = (int)(args.w_stride * 2);
+
+  const int G = gridDim.x;
+  int t_begin = blockIdx.x, t_end = total, t_step = G;
+  if ((G & 7) == 0 && G >= 8) {
+    const int x = blockIdx.x & 7, per = (total + 7) >> 3;
+    t_begin = x * per + (blockIdx.x >> 3);
+    t_end = min(total, (x + 1) * per);
+    t_step = G >> 3;
+  }
+
+  for (int tile = t_begin; tile < t_end; tile += t_step) {
+    int lo = 0, hi = El;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_start[mid] * n_tiles <= tile) lo = mid;
+      else hi = mid;
+    }
+    const int l = lo;
+    const int mt_l = tile_start[l + 1] - tile_start[l];
+    const int local = tile - tile_start[l] * n_tiles;
+    const int nt = local / mt_l, mt = local % mt_l;
+    const int p0 = row_start[l] + mt * BM;
+    const int m_rows = min(BM, row_start[l + 1] - p0);
+    const int n0 = nt * OUT_COLS;
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)l * args.w_stride), (short)0, w_bytes, 0x00020000);
+
+    // this wave's LPW load instructions per stage: byte offset (without k) and LDS offset of each
+    int voff[LPW], loff[LPW];
+    bool isa[LPW];
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int ins = wave * LPW + q;
+      const int r_in = lane / CPR, pos = lane % CPR;
+      if (ins < A_INS) {
+        const int r = ins * RPI + r_in;
+        const int chunk = pos ^ dl_swz<SWZ, CPR>(r);
+        isa[q] = true;
+        loff[q] = ins * 1024;
+        if (r < m_rows) {
+          const int p = p0 + r;
+          const int src = args.a_perm ? args.a_perm[p] : p;
+          voff[q] = src * args.lda * 2 + chunk * 16;
+        } else {
+          voff[q] = OOB;
+        }
+      } else {
+        const int r = (ins - A_INS) * RPI + r_in;
+        const int chunk = pos ^ dl_swz<SWZ, CPR>(r);
+        isa[q] = false;
+        loff[q] = A_BYTES + (ins - A_INS) * 1024;
+        int wrow, ncol;
+        if (GATED) {
+          const int half = r / (BN / 2), rr = r % (BN / 2);
+          ncol = n0 + rr;
+          wrow = ncol + half * args.up_offset;
+        } else {
+          ncol = n0 + r;
+          wrow = ncol;
+        }
+        voff[q] = ncol < args.N ? wrow * args.K * 2 + chunk * 16 : OOB;
+      }
+    }
+    auto issue = [&](int st, int slot) {
+      const int kb = st * BK * 2;
+#pragma unroll
+      for (int q = 0; q < LPW; ++q) {
+        const int vo = voff[q] == OOB ? OOB : voff[q] + kb;
+        auto* dst = (__attribute__((address_space(3))) void*)(smem + slot * STAGE + loff[q]);
+        if (isa[q]) __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, vo, 0, 0, 0);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dst, 16, vo, 0, 0, 0);
+      }
+    };
+
+    typename Op::Acc acc[TM][NACC];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < NACC; ++j)
+#pragma unroll
+        for (int q = 0; q < Op::NR; ++q) acc[i][j][q] = 0.f;
+
+    const int fr = lane & 31, fq = lane >> 5;
+    // fragments of K step kk + 1 are requested before the MFMAs of step kk are issued (two fragment
+    // buffers), so LDS latency overlaps the matrix work of the same wave
+    auto load_frags = [&](const unsigned char* base, int kk, u32x4 (&af)[TM][1], u32x4 (&bfg)[NACC][1]) {
+      const int c = kk / 8 + fq;  // logical 16-byte chunk of this lane's 8 K values
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * WTM + i * S + fr;
+        af[i][0] = ld16(base + r * ROWB + ((c ^ dl_swz<SWZ, CPR>(r)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) {
+        int r;
+        if (GATED) {
+          const int half = j / TN, jj = j % TN;
+          r = half * (BN / 2) + wn * (BN / 2 / WN) + jj * S + fr;
+        } else {
+          r = wn * (BN / WN) + j * S + fr;
+        }
+        bfg[j][0] = ld16(base + A_BYTES + r * ROWB + ((c ^ dl_swz<SWZ, CPR>(r)) << 4));
+      }
+    };
+    auto compute = [&](int slot) {
+      const unsigned char* base = smem + slot * STAGE;
+      constexpr int KSTEPS = BK / Op::KS;
+      u32x4 af[2][TM][1], bfg[2][NACC][1];
+      load_frags(base, 0, af[0], bfg[0]);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        if (ks + 1 < KSTEPS) load_frags(base, (ks + 1) * Op::KS, af[(ks + 1) & 1], bfg[(ks + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[ks & 1][i], bfg[ks & 1][j]);
+      }
+    };
+
+    // earlier stores of this wave are done and every wave is done with the LDS of the previous tile
+    wait_vmcnt<0>();
+    lds_barrier();
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < nk) issue(st, st);
+    for (int s = 0; s < nk; ++s) {
+      // stage s has landed once at most min(NS - 2, nk - 1 - s) younger stages are still in flight
+      const int younger = min(NS - 2, nk - 1 - s);
+      if (NS > 5 && younger >= 4) wait_vmcnt<4 * LPW>();
+      else if (NS > 4 && younger == 3) wait_vmcnt<3 * LPW>();
+      else if (NS > 3 && younger == 2) wait_vmcnt<2 * LPW>();
+      else if (younger == 1) wait_vmcnt<LPW>();
+      else wait_vmcnt<0>();
+      lds_barrier();  // stage s visible to every wave; every wave is done with stage s - 1
+      if (s + NS - 1 < nk) issue(s + NS - 1, (s + NS - 1) % NS);
+      compute(s % NS);
+    }
+
+    // epilogue through LDS, free once every wave is past the last stage: the waves write their bf16
+    // results (lane l holds column l % 32, rows 8*(q/4) + 4*(l/32) + q%4 of each 32x32 block), then
+    // every lane stores whole 16-byte row chunks. Chunk c of tile row r sits at c ^ (4 * ((r >> 2) & 1)),
+    // which puts rows r and r + 4 (written by one instruction) on different LDS banks.
+    constexpr int CPO = OUT_COLS / 8;  // 16-byte chunks per output row
+    static_assert(BM * OUT_COLS * 2 <= NS * STAGE && CPO >= 8, "output tile must fit the stage buffers");
+    auto out_off = [&](int r, int cl) { return r * OUT_COLS * 2 + (((cl >> 3) ^ (((r >> 2) & 1) << 2)) << 4) + (cl & 7) * 2; };
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int cl = GATED ? wn * (BN / 2 / WN) + j * S + fr : wn * (BN / WN) + j * S + fr;
+#pragma unroll
+        for (int q = 0; q < Op::NR; ++q) {
+          const int row = wm * WTM + i * S + Op::out_row(lane, q);
+          float v;
+          if (GATED) v = silu_f32(acc[i][j][q]) * acc[i][j + TN][q];
+          else v = acc[i][j][q];
+          *reinterpret_cast<bf16_t*>(smem + out_off(row, cl)) = (bf16_t)v;
+        }
+      }
+    }
+    lds_barrier();
+    for (int idx = tid; idx < BM * CPO; idx += NW * 64) {
+      const int row = idx / CPO, ch = idx % CPO;
+      const int col = n0 + ch * 8;
+      if (row < m_rows && col < args.N) {
+        const int p = p0 + row;
+        const int orow = args.out_perm ? args.out_perm[p] : p;
+        st16(Out + (int64_t)orow * args.ldo + col, ld16(smem + out_off(row, ch * 8)));
+      }
+    }
+  }
+}
+
 template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT>
 void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
   mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT><<<grid, WM * WN * 64, 0, stream>>>(a);
@@ -414,12 +655,60 @@ void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
 #ifndef MOE_PRE_LDB
 #define MOE_PRE_LDB 2
 #endif
+// direct-to-LDS compute-bound kernel: on/off, LDS row swizzle, grid (workgroups per CU), and its two
+// tile shapes: BM x BN x BK with WM x WN waves and NS LDS stages. The tall (256-row) tile does twice the
+// MFMA work per byte staged and per barrier; it is used when every local expert can hold at least
+// MOE_DL_TALL_MIN_ROWS rows, so the ragged last tile of an expert wastes little.
+#ifndef MOE_PRE_DL
+#define MOE_PRE_DL 1
+#endif
+#ifndef MOE_DL_SWZ
+#define MOE_DL_SWZ 1
+#endif
+#ifndef MOE_DL_WPC
+#define MOE_DL_WPC 1
+#endif
+#ifndef MOE_DL_BK
+#define MOE_DL_BK 64
+#endif
+#ifndef MOE_DL_TALL_MIN_ROWS
+#define MOE_DL_TALL_MIN_ROWS 1024
+#endif
+// 128-row tile
+#ifndef MOE_DL_BN
+#define MOE_DL_BN 256
+#endif
+#ifndef MOE_DL_WM
+#define MOE_DL_WM 2
+#endif
+#ifndef MOE_DL_WN
+#define MOE_DL_WN 4
+#endif
+#ifndef MOE_DL_NS
+#define MOE_DL_NS 3
+#endif
+// 256-row tile
+#ifndef MOE_DLT_BN
+#define MOE_DLT_BN 256
+#endif
+#ifndef MOE_DLT_WM
+#define MOE_DLT_WM 4
+#endif
+#ifndef MOE_DLT_WN
+#define MOE_DLT_WN 2
+#endif
+#ifndef MOE_DLT_NS
+#define MOE_DLT_NS 2
+#endif
 #ifndef MOE_DEC_LDB
 #define MOE_DEC_LDB 1
 #endif
 // few-rows-per-expert (weight streaming) tiles: 32 rows, BN weight rows, BK deep
 #ifndef MOE_DEC_GU_BN
 #define MOE_DEC_GU_BN 128
+#endif
+#ifndef MOE_DEC_NT_MIN_EXPERTS
+#define MOE_DEC_NT_MIN_EXPERTS 16
 #endif
 #ifndef MOE_DEC_GU_BK
 #define MOE_DEC_GU_BK 64
@@ -435,8 +724,10 @@ constexpr int DEC_DN_WN = MOE_DEC_DN_BN / 16 < 4 ? MOE_DEC_DN_BN / 16 : 4;
 using PreOp = MOE_PRE_OP;
 
 
+// wpc = 0: one workgroup per tile of the worst-case tile count (workgroups past the real tile count
+// exit at once) and the hardware dispatcher balances the load
 int persistent_grid(int64_t max_tiles, int num_cus, int wpc) {
-  int64_t g = (int64_t)num_cus * wpc;
+  int64_t g = wpc > 0 ? (int64_t)num_cus * wpc : max_tiles;
   if (max_tiles < g) g = max_tiles;
   if (g >= 8) g &= ~7ll;  // a multiple of the XCD count keeps the XCD-aware order exact
   return (int)(g > 0 ? g : 1);
@@ -446,12 +737,37 @@ int persistent_grid(int64_t max_tiles, int num_cus, int wpc) {
 
 size_t mlp_plan_ints(int El) { return 2 + 2 * (size_t)(El + 1); }
 
-// variant 0: bf16 prefill tiles, 1: bf16 decode tiles (few rows per expert), 2: fp32
-MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int xdt_bf16) {
+namespace {
+// the direct-to-LDS kernel addresses its operands with 31-bit buffer offsets and stages 64-deep K slices
+bool dl_fits(int64_t rows_max, int H, int F) {
+  const int64_t lim = 0x7ffffff0ll - 256;
+  const int64_t send_bytes = rows_max * (int64_t)H * 2, h_bytes = rows_max * (int64_t)F * 2;
+  const int64_t wgu_bytes = (int64_t)2 * F * H * 2, wdn_bytes = (int64_t)H * F * 2;
+  return MOE_PRE_DL && H % MOE_DL_BK == 0 && F % MOE_DL_BK == 0 && send_bytes < lim && h_bytes < lim &&
+         wgu_bytes < lim && wdn_bytes < lim;
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
+               int64_t h_bytes, int num_cus, hipStream_t stream) {
+  const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, BN / 2), num_cus, MOE_DL_WPC);
+  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, true, NS, MOE_DL_SWZ><<<g1, WM * WN * 64, 0, stream>>>(
+      gu, (int)send_bytes);
+  const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, BN), num_cus, MOE_DL_WPC);
+  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, false, NS, MOE_DL_SWZ><<<g2, WM * WN * 64, 0, stream>>>(
+      dn, (int)h_bytes);
+}
+}  // namespace
+
+// variants: 0 bf16 many rows per expert, register-staged; 1 bf16 few rows per expert (weight streaming);
+// 2 fp32; 3 and 4 bf16 many rows per expert, direct-to-LDS with 128- and 256-row tiles
+MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16) {
   if (!xdt_bf16) return MlpTiles{32, 2};
   const int64_t per_expert = El > 0 ? rows_max / El : rows_max;
-  if (per_expert >= 128) return MlpTiles{MOE_PRE_BM, 0};
-  return MlpTiles{32, 1};
+  if (per_expert < 128) return MlpTiles{32, 1};
+  if (!dl_fits(rows_max, H, F)) return MlpTiles{MOE_PRE_BM, 0};
+  if (per_expert >= MOE_DL_TALL_MIN_ROWS) return MlpTiles{256, 4};
+  return MlpTiles{128, 3};
 }
 
 hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
@@ -497,7 +813,15 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   dn.El = El;
 
   switch (tiles.variant) {
-    case 0: {  // bf16, many rows per expert
+    case 3:
+      launch_dl<128, MOE_DL_BN, MOE_DL_WM, MOE_DL_WN, MOE_DL_NS>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
+                                                                 rows_max * (int64_t)F * 2, num_cus, stream);
+      break;
+    case 4:
+      launch_dl<256, MOE_DLT_BN, MOE_DLT_WM, MOE_DLT_WN, MOE_DLT_NS>(
+          gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
+      break;
+    case 0: {  // bf16, many rows per expert, operands staged through registers
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_PRE_BN / 2), num_cus, MOE_PRE_WPC);
       launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB, false>(gu, g1, stream);
       const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_PRE_BN), num_cus, MOE_PRE_WPC);
@@ -508,7 +832,7 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
       // with many local experts of few rows each, streaming (non-temporal) weight loads in the gate/up
       // pass measured faster; with few experts the default cache policy did
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_DEC_GU_BN / 2), num_cus, MOE_DEC_WPC);
-      if (El >= 16)
+      if (El >= MOE_DEC_NT_MIN_EXPERTS)
         launch_gemm<bf16_t, Op16, 32, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true>(
             gu, g1, stream);
       else

@@ -245,6 +245,10 @@ EDGE = [
     ("E512_k8", 300, 64, 512, 8, 32, 8, 5, "bf16", "zipf"),
     ("hot_overflow", 512, 128, 64, 6, 64, 1, 48, "bf16", "hot8"),
     ("many_rows_tile_edges", 700, 128, 4, 2, 160, 1, 300, "bf16", "uniform"),
+    # direct-to-LDS grouped GEMM: 128-row tiles (400 rows per expert), then 256-row tiles (2200 rows per
+    # local expert); F = 192 and H = 192 / 320 leave a ragged last column tile in both GEMMs
+    ("dl128_ragged", 900, 192, 4, 2, 192, 1, 400, "bf16", "zipf"),
+    ("dl256_ragged_R2", 2600, 320, 4, 2, 192, 2, 1100, "bf16", "zipf"),
 ]
 
 
