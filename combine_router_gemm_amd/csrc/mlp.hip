@@ -703,7 +703,13 @@ void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
 #ifndef MOE_DEC_LDB
 #define MOE_DEC_LDB 1
 #endif
-// few-rows-per-expert (weight streaming) tiles: 32 rows, BN weight rows, BK deep
+// few-rows-per-expert (weight streaming) tiles: 32 or 64 rows, BN weight rows, BK deep. 64-row tiles
+// are used when the capacity per local expert is at least MOE_DEC_TALL_MIN_ROWS rows: an expert then
+// often holds more than 32 rows, and one 64-row tile streams its weights once where two 32-row tiles
+// would stream them twice.
+#ifndef MOE_DEC_TALL_MIN_ROWS
+#define MOE_DEC_TALL_MIN_ROWS 32
+#endif
 #ifndef MOE_DEC_GU_BN
 #define MOE_DEC_GU_BN 128
 #endif
@@ -757,14 +763,32 @@ void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H
   mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, false, NS, MOE_DL_SWZ><<<g2, WM * WN * 64, 0, stream>>>(
       dn, (int)h_bytes);
 }
+
+template <int BM>
+void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int El, int num_cus,
+                   hipStream_t stream) {
+  // with many local experts of few rows each, streaming (non-temporal) weight loads in the gate/up
+  // pass measured faster; with few experts the default cache policy did
+  const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_DEC_GU_BN / 2), num_cus, MOE_DEC_WPC);
+  if (El >= MOE_DEC_NT_MIN_EXPERTS)
+    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true>(
+        gu, g1, stream);
+  else
+    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, false>(
+        gu, g1, stream);
+  const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
+  launch_gemm<bf16_t, Op16, BM, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB, false>(
+      dn, g2, stream);
+}
 }  // namespace
 
-// variants: 0 bf16 many rows per expert, register-staged; 1 bf16 few rows per expert (weight streaming);
-// 2 fp32; 3 and 4 bf16 many rows per expert, direct-to-LDS with 128- and 256-row tiles
+// variants: 0 bf16 many rows per expert, register-staged; 1 and 5 bf16 few rows per expert (weight
+// streaming) with 32- and 64-row tiles; 2 fp32; 3 and 4 bf16 many rows per expert, direct-to-LDS with
+// 128- and 256-row tiles
 MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16) {
   if (!xdt_bf16) return MlpTiles{32, 2};
   const int64_t per_expert = El > 0 ? rows_max / El : rows_max;
-  if (per_expert < 128) return MlpTiles{32, 1};
+  if (per_expert < 128) return per_expert >= MOE_DEC_TALL_MIN_ROWS ? MlpTiles{64, 5} : MlpTiles{32, 1};
   if (!dl_fits(rows_max, H, F)) return MlpTiles{MOE_PRE_BM, 0};
   if (per_expert >= MOE_DL_TALL_MIN_ROWS) return MlpTiles{256, 4};
   return MlpTiles{128, 3};
@@ -828,21 +852,12 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
       launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, false, MOE_PRE_RS, MOE_PRE_LDB, false>(dn, g2, stream);
       break;
     }
-    case 1: {  // bf16, few rows per expert: stream the weights through 32-row tiles
-      // with many local experts of few rows each, streaming (non-temporal) weight loads in the gate/up
-      // pass measured faster; with few experts the default cache policy did
-      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_DEC_GU_BN / 2), num_cus, MOE_DEC_WPC);
-      if (El >= MOE_DEC_NT_MIN_EXPERTS)
-        launch_gemm<bf16_t, Op16, 32, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true>(
-            gu, g1, stream);
-      else
-        launch_gemm<bf16_t, Op16, 32, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, false>(
-            gu, g1, stream);
-      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
-      launch_gemm<bf16_t, Op16, 32, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB, false>(
-          dn, g2, stream);
+    case 1:  // bf16, few rows per expert: stream the weights through 32- or 64-row tiles
+      launch_decode<32>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
       break;
-    }
+    case 5:
+      launch_decode<64>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
+      break;
     default: {  // fp32
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus, 2);
       launch_gemm<float, OpF32, 32, 64, 32, 1, 2, true, 2, 2, false>(gu, g1, stream);

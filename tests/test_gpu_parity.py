@@ -249,6 +249,8 @@ EDGE = [
     # local expert); F = 192 and H = 192 / 320 leave a ragged last column tile in both GEMMs
     ("dl128_ragged", 900, 192, 4, 2, 192, 1, 400, "bf16", "zipf"),
     ("dl256_ragged_R2", 2600, 320, 4, 2, 192, 2, 1100, "bf16", "zipf"),
+    # 64-row weight-streaming tiles (capacity 75 rows per expert on average), hot experts over 64 rows
+    ("dec64_multi_mtile", 300, 128, 8, 2, 96, 1, 100, "bf16", "zipf"),
 ]
 
 
