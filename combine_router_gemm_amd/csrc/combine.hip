@@ -37,7 +37,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out_
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       raw[i][j] = u32x4{0u, 0u, 0u, 0u};
-      if (v < nvec && j < k && s_row[j] >= 0) raw[i][j] = ld16(out_buf + (int64_t)s_row[j] * H + (int64_t)v * VN);
+      if (v < nvec && j < k && s_row[j] >= 0) {
+        const T* src = out_buf + (int64_t)s_row[j] * H + (int64_t)v * VN;
+        raw[i][j] = ld16_nt(src);  // each expert-output row is read once: streaming loads measured faster
+      }
     }
   }
 #pragma unroll

@@ -19,9 +19,9 @@
 //                    pair's rank inside its block (to pair_local).
 //   dispatch_scan    one workgroup: per expert, an exclusive scan of blk_count over blocks (in place),
 //                    count / kept / overflow, then an exclusive scan of kept over experts -> offsets.
-//   dispatch_scatter workgroups of 256 threads over (token, 16-byte column slices): position = block
-//                    base + rank in block; kept pairs write the layout entries, and each slice of the
-//                    token row is read once and stored to every kept row (non-temporal stores).
+//   dispatch_scatter one wave per token: position = block base + rank in block; kept pairs write the
+//                    layout entries, and each 16-byte slice of the token row is read once and stored to
+//                    every kept row (non-temporal stores).
 #include "common.h"
 #include "kernels.h"
 
@@ -149,69 +149,66 @@ __global__ __launch_bounds__(DS_THREADS) void dispatch_scan_kernel(int* __restri
   if (e == E - 1) offset[E] = wbase + incl;
 }
 
-// grid: T * chunks workgroups of 256 threads. Workgroup (t, c): its first k threads resolve the
-// positions of token t's pairs (chunk 0 also writes the layout entries), then every thread copies VPT
-// 16-byte column slices of x[t] (c*256*VPT + i*256 + tid) to each kept row.
-template <typename T, int VPT>
-__global__ __launch_bounds__(256) void dispatch_scatter_kernel(const T* __restrict__ x, const int* __restrict__ ids,
-                                                              int H, int k, int E, int C, int chunks,
-                                                              const int* __restrict__ blk_base,
-                                                              const int* __restrict__ pair_local,
-                                                              const int* __restrict__ offset,
-                                                              int* __restrict__ row_token, int* __restrict__ row_slot,
-                                                              int* __restrict__ pair_row, T* __restrict__ send_buf) {
-  __shared__ int s_row[MOE_MAX_TOPK];
-  const int t = blockIdx.x / chunks;
-  const int c = blockIdx.x % chunks;
-  const int tid = threadIdx.x;
-  if (tid < k) {
-    const int64_t p = (int64_t)t * k + tid;
+// One wave per token, SCATTER_WAVES tokens per workgroup. Lanes j < k resolve the rows of pairs
+// (t, j) and write their layout entries; the kept rows are shared through a ballot and lane reads (no
+// workgroup barrier). Each lane then has VPL 16-byte column slices of x[t] in flight at once
+// (lane + 64 i, one pass per 64 * VPL slices) and stores each to every kept row with non-temporal
+// stores. A token whose pairs were all dropped is not read.
+constexpr int SCATTER_WAVES = 4;
+
+template <typename T, int VPL>
+__global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_kernel(
+    const T* __restrict__ x, const int* __restrict__ ids, int T_, int H, int k, int E, int C,
+    const int* __restrict__ blk_base, const int* __restrict__ pair_local, const int* __restrict__ offset,
+    int* __restrict__ row_token, int* __restrict__ row_slot, int* __restrict__ pair_row, T* __restrict__ send_buf) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * SCATTER_WAVES + (int)(threadIdx.x >> 6);
+  if (t >= T_) return;
+  int row = -1;
+  if (lane < k) {
+    const int64_t p = (int64_t)t * k + lane;
     const int e = ids[p];
     const int local = pair_local[p];
-    int row = -1;
     if (e >= 0 && e < E && local >= 0) {
       const int pos = blk_base[(int64_t)(t / DISPATCH_TB) * E + e] + local;
       if (pos < C) row = offset[e] + pos;
     }
-    s_row[tid] = row;
-    if (c == 0) {
-      pair_row[p] = row;
-      if (row >= 0) {
-        row_token[row] = t;
-        row_slot[row] = tid;
-      }
+    pair_row[p] = row;
+    if (row >= 0) {
+      row_token[row] = t;
+      row_slot[row] = lane;
     }
   }
-  __syncthreads();
-  bool any = false;
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) any |= (j < k && s_row[j] >= 0);
-  if (!any) return;  // every pair of this token was dropped: nothing to copy
+  uint64_t kept = __ballot(row >= 0);  // only lanes < k can hold a row
+  if (kept == 0) return;               // every pair of this token was dropped: nothing to copy
   constexpr int VN = Vec<T>::N;
   const int nvec = H / VN;
-  const int v0 = c * 256 * VPT + tid;
-  u32x4 val[VPT];
+  const T* src = x + (int64_t)t * H;
+  for (int base = 0; base < nvec; base += 64 * VPL) {
+    u32x4 val[VPL];
 #pragma unroll
-  for (int i = 0; i < VPT; ++i)
-    if (v0 + i * 256 < nvec) val[i] = ld16(x + (int64_t)t * H + (int64_t)(v0 + i * 256) * VN);
+    for (int i = 0; i < VPL; ++i) {
+      const int v = base + lane + i * 64;
+      if (v < nvec) val[i] = ld16(src + (int64_t)v * VN);
+    }
+    for (uint64_t m = kept; m; m &= m - 1) {
+      const int j = __builtin_ctzll(m);
+      T* dst = send_buf + (int64_t)__shfl(row, j, 64) * H;
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    if (j < k && s_row[j] >= 0) {
-      T* dst = send_buf + (int64_t)s_row[j] * H;
-#pragma unroll
-      for (int i = 0; i < VPT; ++i)
-        if (v0 + i * 256 < nvec) st16_nt(dst + (int64_t)(v0 + i * 256) * VN, val[i]);
+      for (int i = 0; i < VPL; ++i) {
+        const int v = base + lane + i * 64;
+        if (v < nvec) st16_nt(dst + (int64_t)v * VN, val[i]);
+      }
     }
   }
 }
 
-template <typename T, int VPT>
+template <typename T, int VPL>
 void launch_scatter_t(const void* x, const int* ids, const moe_layout_t& L, void* send_buf, const int* blk_base,
                       const int* pair_local, hipStream_t stream) {
-  const int chunks = ceil_div_host(L.H / Vec<T>::N, 256 * VPT);
-  const unsigned blocks = (unsigned)((int64_t)L.T * chunks);
-  dispatch_scatter_kernel<T, VPT><<<blocks, 256, 0, stream>>>(
-      static_cast<const T*>(x), ids, L.H, L.k, L.E, L.C, chunks, blk_base, pair_local, L.expert_offset, L.row_token,
+  const unsigned blocks = (unsigned)ceil_div_host(L.T, SCATTER_WAVES);
+  dispatch_scatter_kernel<T, VPL><<<blocks, SCATTER_WAVES * 64, 0, stream>>>(
+      static_cast<const T*>(x), ids, L.T, L.H, L.k, L.E, L.C, blk_base, pair_local, L.expert_offset, L.row_token,
       L.row_slot, L.pair_row, static_cast<T*>(send_buf));
 }
 
@@ -227,15 +224,16 @@ hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const mo
   dispatch_scan_kernel<<<1, DS_THREADS, 0, stream>>>(blk_count, nblk, L.E, L.C, L.expert_count, L.expert_kept,
                                                      L.expert_overflow, L.expert_offset);
   if (L.T == 0) return hipGetLastError();
+  // slices per lane in flight: enough for the whole row in one pass up to 1024 slices (bf16 H <= 8192)
   const int nvec = L.H / (xdt_bf16 ? 8 : 4);
-  const int vpt = nvec >= 768 ? 4 : (nvec >= 384 ? 2 : 1);
+  const int vpl = nvec > 256 ? 16 : (nvec > 64 ? 4 : 1);
   if (xdt_bf16) {
-    if (vpt == 4) launch_scatter_t<bf16_t, 4>(x, ids, L, send_buf, blk_count, pair_local, stream);
-    else if (vpt == 2) launch_scatter_t<bf16_t, 2>(x, ids, L, send_buf, blk_count, pair_local, stream);
+    if (vpl == 16) launch_scatter_t<bf16_t, 16>(x, ids, L, send_buf, blk_count, pair_local, stream);
+    else if (vpl == 4) launch_scatter_t<bf16_t, 4>(x, ids, L, send_buf, blk_count, pair_local, stream);
     else launch_scatter_t<bf16_t, 1>(x, ids, L, send_buf, blk_count, pair_local, stream);
   } else {
-    if (vpt == 4) launch_scatter_t<float, 4>(x, ids, L, send_buf, blk_count, pair_local, stream);
-    else if (vpt == 2) launch_scatter_t<float, 2>(x, ids, L, send_buf, blk_count, pair_local, stream);
+    if (vpl == 16) launch_scatter_t<float, 16>(x, ids, L, send_buf, blk_count, pair_local, stream);
+    else if (vpl == 4) launch_scatter_t<float, 4>(x, ids, L, send_buf, blk_count, pair_local, stream);
     else launch_scatter_t<float, 1>(x, ids, L, send_buf, blk_count, pair_local, stream);
   }
   return hipGetLastError();
