@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times), the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters, and exit")
+    ap.add_argument("--calibrate-gemm", action="store_true",
+                    help="only time the vendor library's bf16 batched GEMM (hipBLASLt through torch.bmm, contiguous "
+                         "operands) on the workload's expert-GEMM shapes and on an 8192^3 GEMM, and exit: the "
+                         "practical MFMA ceiling of this machine, for context")
     return ap.parse_args()
 
 
@@ -85,6 +89,48 @@ def calibrate_copy(mib: int) -> None:
     torch.cuda.synchronize()
     print(json.dumps({"calibration": "device-to-device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n,
                       "copies": 3}), flush=True)
+
+
+def calibrate_gemm(cfg, reps: int = 20) -> None:
+    """Vendor-library reference: hipBLASLt bf16 GEMMs (torch.bmm / torch.mm, contiguous operands) with the
+    shapes of the workload's two expert GEMMs, El experts x (capacity rows per local expert), without the
+    row gather, the fused SwiGLU and the row scatter the expert MLP does."""
+    import torch
+    import moe_workloads as W
+
+    dev = torch.device("cuda:0")
+    C = W.capacity(cfg, cfg.T)
+    M = max(1, W.rows_max(cfg.T, cfg.k, cfg.E, C) // cfg.El)
+    El, H, F = cfg.El, cfg.H, cfg.F
+
+    def timed(fn, flops, case):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        print(json.dumps({"calibration": "vendor bf16 GEMM", "case": case, "us": round(us, 1),
+                          "TFLOP/s": round(flops / us / 1e6, 1),
+                          "frac_of_peak": round(flops / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}), flush=True)
+
+    bf = torch.bfloat16
+    a = torch.randn(El, M, H, device=dev, dtype=bf)
+    wgu = torch.randn(El, H, 2 * F, device=dev, dtype=bf)
+    h = torch.randn(El, M, F, device=dev, dtype=bf)
+    wdn = torch.randn(El, F, H, device=dev, dtype=bf)
+    o1 = torch.empty(El, M, 2 * F, device=dev, dtype=bf)
+    o2 = torch.empty(El, M, H, device=dev, dtype=bf)
+    timed(lambda: torch.bmm(a, wgu, out=o1), 2 * El * M * H * 2 * F, f"{cfg.name} gate/up {El}x[{M}x{H}]x[{H}x{2 * F}]")
+    timed(lambda: torch.bmm(h, wdn, out=o2), 2 * El * M * F * H, f"{cfg.name} down {El}x[{M}x{F}]x[{F}x{H}]")
+    del a, wgu, h, wdn, o1, o2
+    x = torch.randn(8192, 8192, device=dev, dtype=bf)
+    y = torch.randn(8192, 8192, device=dev, dtype=bf)
+    timed(lambda: torch.mm(x, y), 2 * 8192 ** 3, "square 8192^3")
 
 
 def pick_workload(name):
@@ -159,6 +205,11 @@ def main():
 
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)
+        return
+    if args.calibrate_gemm:
+        import torch
+        torch.cuda.set_device(0)
+        calibrate_gemm(pick_workload(args.workload))
         return
 
     import torch

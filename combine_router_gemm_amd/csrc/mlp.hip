@@ -401,7 +401,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool GATED, int NS, int SWZ>
+template <int BM, int BN, int BK, int WM, int WN, bool GATED, int NS, int SWZ, bool SPREAD, bool FENCE>
 __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args, int a_bytes) {
   using Op = Op32;
   static_assert(BK == 32 || BK == 64, "32- or 64-deep stages");
@@ -501,16 +501,19 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
         voff[q] = ncol < args.N ? wrow * args.K * 2 + chunk * 16 : OOB;
       }
     }
-    auto issue = [&](int st, int slot) {
+    // issue this wave's loads q with q % parts == part of stage st into LDS slot `slot`
+    auto issue_part = [&](int st, int slot, int part, int parts) {
       const int kb = st * BK * 2;
 #pragma unroll
       for (int q = 0; q < LPW; ++q) {
+        if (q % parts != part) continue;
         const int vo = voff[q] == OOB ? OOB : voff[q] + kb;
         auto* dst = (__attribute__((address_space(3))) void*)(smem + slot * STAGE + loff[q]);
         if (isa[q]) __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, vo, 0, 0, 0);
         else __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dst, 16, vo, 0, 0, 0);
       }
     };
+    auto issue = [&](int st, int slot) { issue_part(st, slot, 0, 1); };
 
     typename Op::Acc acc[TM][NACC];
 #pragma unroll
@@ -542,18 +545,24 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
         bfg[j][0] = ld16(base + A_BYTES + r * ROWB + ((c ^ dl_swz<SWZ, CPR>(r)) << 4));
       }
     };
-    auto compute = [&](int slot) {
+    // the loads of stage `next` (into slot next_slot, if next >= 0) are spread over the K steps, so
+    // the address units and LDS writes of every wave do not all burst right after the barrier
+    auto compute = [&](int slot, int next, int next_slot) {
       const unsigned char* base = smem + slot * STAGE;
       constexpr int KSTEPS = BK / Op::KS;
       u32x4 af[2][TM][1], bfg[2][NACC][1];
       load_frags(base, 0, af[0], bfg[0]);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
+        if (SPREAD && next >= 0) issue_part(next, next_slot, ks, KSTEPS);
+        if (!SPREAD && next >= 0 && ks == 0) issue(next, next_slot);
         if (ks + 1 < KSTEPS) load_frags(base, (ks + 1) * Op::KS, af[(ks + 1) & 1], bfg[(ks + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[ks & 1][i], bfg[ks & 1][j]);
+        // keep the scheduler from hoisting later steps' fragment reads (register pressure)
+        if (FENCE) __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -572,8 +581,8 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
       else if (younger == 1) wait_vmcnt<LPW>();
       else wait_vmcnt<0>();
       lds_barrier();  // stage s visible to every wave; every wave is done with stage s - 1
-      if (s + NS - 1 < nk) issue(s + NS - 1, (s + NS - 1) % NS);
-      compute(s % NS);
+      const int next = s + NS - 1 < nk ? s + NS - 1 : -1;
+      compute(s % NS, next, next >= 0 ? next % NS : 0);
     }
 
     // epilogue through LDS, free once every wave is past the last stage: the waves write their bf16
@@ -687,6 +696,12 @@ void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
 #ifndef MOE_DL_NS
 #define MOE_DL_NS 3
 #endif
+#ifndef MOE_DL_SPREAD
+#define MOE_DL_SPREAD true
+#endif
+#ifndef MOE_DL_FENCE
+#define MOE_DL_FENCE false
+#endif
 // 256-row tile
 #ifndef MOE_DLT_BN
 #define MOE_DLT_BN 256
@@ -699,6 +714,9 @@ void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
 #endif
 #ifndef MOE_DLT_NS
 #define MOE_DLT_NS 2
+#endif
+#ifndef MOE_DLT_SPREAD
+#define MOE_DLT_SPREAD false
 #endif
 #ifndef MOE_DEC_LDB
 #define MOE_DEC_LDB 1
@@ -753,14 +771,14 @@ bool dl_fits(int64_t rows_max, int H, int F) {
          wgu_bytes < lim && wdn_bytes < lim;
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, bool SPREAD>
 void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
                int64_t h_bytes, int num_cus, hipStream_t stream) {
   const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, BN / 2), num_cus, MOE_DL_WPC);
-  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, true, NS, MOE_DL_SWZ><<<g1, WM * WN * 64, 0, stream>>>(
+  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, true, NS, MOE_DL_SWZ, SPREAD, MOE_DL_FENCE><<<g1, WM * WN * 64, 0, stream>>>(
       gu, (int)send_bytes);
   const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, BN), num_cus, MOE_DL_WPC);
-  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, false, NS, MOE_DL_SWZ><<<g2, WM * WN * 64, 0, stream>>>(
+  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, false, NS, MOE_DL_SWZ, SPREAD, MOE_DL_FENCE><<<g2, WM * WN * 64, 0, stream>>>(
       dn, (int)h_bytes);
 }
 
@@ -838,11 +856,11 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
 
   switch (tiles.variant) {
     case 3:
-      launch_dl<128, MOE_DL_BN, MOE_DL_WM, MOE_DL_WN, MOE_DL_NS>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
+      launch_dl<128, MOE_DL_BN, MOE_DL_WM, MOE_DL_WN, MOE_DL_NS, MOE_DL_SPREAD>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
                                                                  rows_max * (int64_t)F * 2, num_cus, stream);
       break;
     case 4:
-      launch_dl<256, MOE_DLT_BN, MOE_DLT_WM, MOE_DLT_WN, MOE_DLT_NS>(
+      launch_dl<256, MOE_DLT_BN, MOE_DLT_WM, MOE_DLT_WN, MOE_DLT_NS, MOE_DLT_SPREAD>(
           gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
       break;
     case 0: {  // bf16, many rows per expert, operands staged through registers
