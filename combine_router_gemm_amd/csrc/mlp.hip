@@ -133,6 +133,10 @@ __global__ __launch_bounds__(PLAN_THREADS) void mlp_plan_kernel(const int* __res
 // ------------------------------------------------------------------------------------------------
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
+#ifndef MOE_GEMM_MIN_WAVES
+#define MOE_GEMM_MIN_WAVES 1
+#endif
+
 struct GemmArgs {
   const void* A;        // activations: send_buf (gate/up) or h (down)
   int lda;              // row length of A (= K)
@@ -147,13 +151,17 @@ struct GemmArgs {
   const int* out_perm;  // scatter map for output rows (down) or nullptr (plan order)
   const int* plan;
   int El;
+  int a_bytes;          // bytes of A (rows_max x lda elements) when it fits 31-bit buffer offsets, else 0
+  int w_bytes;          // bytes of one expert's weights (w_stride elements), same rule
 };
 
 // BM x BN tile, BK-deep LDS stages, WM x WN waves, MFMA op Op. GATED: the B tile holds BN/2 gate rows
 // then the BN/2 up rows of the same output columns, and each wave owns matching gate and up
 // accumulators.
-template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT>
-__global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
+template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
+          bool BUF>
+__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(MOE_GEMM_MIN_WAVES)))
+void mlp_gemm_kernel(GemmArgs args) {
   constexpr int NTH = WM * WN * 64;
   constexpr int VN = Vec<T>::N;           // elements per 16-byte vector
   constexpr int PAD = 16 / sizeof(T);     // one vector of padding per LDS row
@@ -182,6 +190,9 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
   const T* __restrict__ A = static_cast<const T*>(args.A);
   const T* __restrict__ W = static_cast<const T*>(args.W);
   T* __restrict__ Out = static_cast<T*>(args.Out);
+  constexpr int A_OOB = 0x7ffffff0;
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, BUF ? args.a_bytes : 0, 0x00020000);
   const int El = args.El;
   const int* row_start = args.plan + 2;
   const int* tile_start = args.plan + 3 + El;
@@ -226,7 +237,11 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
     // valid address (rows past the tile end read the tile's first row, columns past K read the last
     // vector of the row) and masked to zero when it is written to LDS: a load under a branch would
     // make the compiler wait for every load in flight before the registers are reused.
+    // BUF: A and W are read with buffer loads (32-bit offsets instead of 64-bit pointers), and rows
+    // past the tile or past N use an offset past the buffer, which the hardware answers with zeros and
+    // no memory request (a tile of an expert with few rows then moves only its real rows)
     const T* a_src[A_VEC];
+    int a_off[A_VEC];
     int a_lds[A_VEC];
     bool a_ok[A_VEC];
 #pragma unroll
@@ -238,10 +253,14 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
       const int p = p0 + (a_ok[i] ? r : 0);
       const int src_row = args.a_perm ? args.a_perm[p] : p;
       a_src[i] = A + (int64_t)src_row * args.lda;
+      a_off[i] = (BUF && a_ok[i]) ? src_row * args.lda * (int)sizeof(T) : A_OOB;  // < a_bytes when BUF
     }
     const T* b_src[B_VEC];
+    int b_off[B_VEC];
     int b_lds[B_VEC];
     bool b_ok[B_VEC];
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Wl, (short)0, BUF ? args.w_bytes : 0, 0x00020000);
 #pragma unroll
     for (int i = 0; i < B_VEC; ++i) {
       const int idx = tid + i * NTH;
@@ -258,6 +277,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
       }
       b_ok[i] = ncol < args.N;
       b_src[i] = Wl + (int64_t)(b_ok[i] ? wrow : 0) * args.K;
+      b_off[i] = (BUF && b_ok[i]) ? wrow * args.K * (int)sizeof(T) : A_OOB;  // < w_bytes when BUF
     }
 
     typename Op::Acc acc[TM][NACC];
@@ -276,13 +296,27 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_kernel(GemmArgs args) {
     auto load_stage = [&](int st, u32x4 (&xa)[A_VEC], u32x4 (&xb)[B_VEC]) {
       const int k0 = st * BK;
 #pragma unroll
-      for (int i = 0; i < A_VEC; ++i) xa[i] = ld16(a_src[i] + min(k0 + a_lds[i] % LDR, args.K - VN));
+      for (int i = 0; i < A_VEC; ++i) {
+        const int col = min(k0 + a_lds[i] % LDR, args.K - VN);
+        if (BUF) {
+          const int vo = a_off[i] == A_OOB ? A_OOB : a_off[i] + col * (int)sizeof(T);
+          xa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, vo, 0, 0));
+        } else {
+          xa[i] = ld16(a_src[i] + col);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < B_VEC; ++i) {
         // weights are read once per tile: streaming (non-temporal) loads keep the reused activation
         // rows resident in L2 when many tiles share them
-        const T* pb = b_src[i] + min(k0 + b_lds[i] % LDR, args.K - VN);
-        xb[i] = BNT ? ld16_nt(pb) : ld16(pb);
+        const int col = min(k0 + b_lds[i] % LDR, args.K - VN);
+        if (BUF) {
+          const int vo = b_off[i] == A_OOB ? A_OOB : b_off[i] + col * (int)sizeof(T);
+          xb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, vo, 0, BNT ? 2 : 0));
+        } else {
+          const T* pb = b_src[i] + col;
+          xb[i] = BNT ? ld16_nt(pb) : ld16(pb);
+        }
       }
     };
     auto store_stage = [&](int st, int buf, const u32x4 (&xa)[A_VEC], const u32x4 (&xb)[B_VEC]) {
@@ -623,7 +657,10 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
 
 template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT>
 void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
-  mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT><<<grid, WM * WN * 64, 0, stream>>>(a);
+  if (a.a_bytes > 0 && a.w_bytes > 0)
+    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, true><<<grid, WM * WN * 64, 0, stream>>>(a);
+  else
+    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, false><<<grid, WM * WN * 64, 0, stream>>>(a);
 }
 
 // Persistent grid sizes in workgroups per CU and the compute-bound tile shapes; overridable at compile
@@ -750,6 +787,9 @@ using PreOp = MOE_PRE_OP;
 
 // wpc = 0: one workgroup per tile of the worst-case tile count (workgroups past the real tile count
 // exit at once) and the hardware dispatcher balances the load
+// a buffer's byte size when 31-bit buffer offsets (with room for the out-of-range marker) cover it, else 0
+int buffer_bytes(int64_t bytes) { return bytes > 0 && bytes < 0x7ffffff0ll - 256 ? (int)bytes : 0; }
+
 int persistent_grid(int64_t max_tiles, int num_cus, int wpc) {
   int64_t g = wpc > 0 ? (int64_t)num_cus * wpc : max_tiles;
   if (max_tiles < g) g = max_tiles;
@@ -838,6 +878,8 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   gu.out_perm = nullptr;
   gu.plan = plan;
   gu.El = El;
+  gu.a_bytes = buffer_bytes(rows_max * H * (xdt_bf16 ? 2 : 4));
+  gu.w_bytes = buffer_bytes(gu.w_stride * (xdt_bf16 ? 2 : 4));
 
   GemmArgs dn{};
   dn.A = hbuf;
@@ -853,6 +895,8 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   dn.out_perm = perm;
   dn.plan = plan;
   dn.El = El;
+  dn.a_bytes = buffer_bytes(rows_max * F * (xdt_bf16 ? 2 : 4));
+  dn.w_bytes = buffer_bytes(dn.w_stride * (xdt_bf16 ? 2 : 4));
 
   switch (tiles.variant) {
     case 3:
