@@ -17,6 +17,7 @@ struct RouteTiles {
   int BM, BN;
 };
 RouteTiles route_tiles(int T, int xdt_bf16);
+bool route_fused(int T, int E);  // one fused kernel, no workspace
 int route_splits(int T, int H, int E, int xdt_bf16, int num_cus);
 int route_k_split(int H, int splits);
 hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, const float* bias,

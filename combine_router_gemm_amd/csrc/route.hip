@@ -1,4 +1,5 @@
 // Router: logits = x W_r^T (+ bias) in fp32, then per-token top-k and softmax over the k selected.
+// Few experts and tokens (E <= 16, T <= 4096) take one fused kernel (route_small); otherwise:
 //
 // The router is a small linear layer scoring every expert; the k best experts are chosen and their
 // weights come from the router's distribution ("Efficient and portable mixture-of-experts
@@ -19,6 +20,13 @@
 namespace moe {
 
 namespace {
+
+#ifndef ROUTE_MAX_SPLITS
+#define ROUTE_MAX_SPLITS 16
+#endif
+#ifndef ROUTE_FUSED_MAX_T
+#define ROUTE_FUSED_MAX_T 4096
+#endif
 
 constexpr int RG_BM = 64;   // tokens per tile
 constexpr int RG_BN = 64;   // experts per tile
@@ -269,57 +277,11 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
   return (v > bv) || (v == bv && e < be);
 }
 
-// G lanes per token (power of two, 8..64), V = ceil(E / G) logits per lane, expert of lane g's
-// i-th value is i * G + g.
-template <int G>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, int splits,
-                                                         const float* __restrict__ bias, int64_t bias_stride,
-                                                         int T, int E, int k, float* logits,
-                                                         int* __restrict__ topk_ids, float* __restrict__ topk_w) {
-  // G < 64 is only chosen when E <= G (one logit per lane); G == 64 covers E <= 512 (8 per lane)
-  constexpr int VMAX = G < 64 ? 1 : MOE_MAX_EXPERTS / 64;
-  const int g = threadIdx.x & (G - 1);
-  const int t = (blockIdx.x * blockDim.x + threadIdx.x) / G;
-  const bool live = t < T;
-  const int V = (E + G - 1) / G;
-
-  float val[VMAX];
-  bool taken[VMAX];
-  float sum[VMAX];
-#pragma unroll
-  for (int i = 0; i < VMAX; ++i) {
-    const int e = i * G + g;
-    taken[i] = !(i < V && e < E && live);
-    sum[i] = taken[i] ? 0.f : partial[(int64_t)t * E + e];
-  }
-  // the remaining K-split partials, four splits of loads in flight at a time, added in split order
-  const int64_t TE = (int64_t)T * E;
-  for (int sp0 = 1; sp0 < splits; sp0 += 4) {
-    float tmp[4][VMAX];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < VMAX; ++i)
-        tmp[u][i] = (!taken[i] && sp0 + u < splits) ? partial[(sp0 + u) * TE + (int64_t)t * E + i * G + g] : 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < VMAX; ++i)
-        if (sp0 + u < splits) sum[i] += tmp[u][i];
-  }
-#pragma unroll
-  for (int i = 0; i < VMAX; ++i) {
-    val[i] = -INFINITY;
-    if (!taken[i]) {
-      const int e = i * G + g;
-      float s = sum[i];
-      if (bias) s += bias[(int64_t)t * bias_stride + e];
-      logits[(int64_t)t * E + e] = s;
-      s = s + 0.0f;                       // -0 -> +0: equal values compare equal either way
-      val[i] = (s == s) ? s : -INFINITY;  // NaN ranks as -inf
-    }
-  }
-
+// k rounds of a butterfly arg-max over G lanes (lane g holds the values of experts i * G + g; taken
+// marks values out of the running), then the softmax over the k winners; lanes g < k write slot g.
+template <int G, int VMAX>
+__device__ __forceinline__ void select_topk(const float (&val)[VMAX], bool (&taken)[VMAX], int g, int t, bool live,
+                                            int k, int* __restrict__ topk_ids, float* __restrict__ topk_w) {
   float sel_v[MOE_MAX_TOPK];
   int sel_e[MOE_MAX_TOPK];
 #pragma unroll
@@ -376,6 +338,128 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, i
   }
 }
 
+// G lanes per token (power of two, 8..64), V = ceil(E / G) logits per lane, expert of lane g's
+// i-th value is i * G + g.
+template <int G>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, int splits,
+                                                         const float* __restrict__ bias, int64_t bias_stride,
+                                                         int T, int E, int k, float* logits,
+                                                         int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  // G < 64 is only chosen when E <= G (one logit per lane); G == 64 covers E <= 512 (8 per lane)
+  constexpr int VMAX = G < 64 ? 1 : MOE_MAX_EXPERTS / 64;
+  const int g = threadIdx.x & (G - 1);
+  const int t = (blockIdx.x * blockDim.x + threadIdx.x) / G;
+  const bool live = t < T;
+  const int V = (E + G - 1) / G;
+
+  float val[VMAX];
+  bool taken[VMAX];
+  float sum[VMAX];
+#pragma unroll
+  for (int i = 0; i < VMAX; ++i) {
+    const int e = i * G + g;
+    taken[i] = !(i < V && e < E && live);
+    sum[i] = taken[i] ? 0.f : partial[(int64_t)t * E + e];
+  }
+  // the remaining K-split partials, SPF splits of loads in flight at a time, added in split order
+  constexpr int SPF = 8;
+  const int64_t TE = (int64_t)T * E;
+  for (int sp0 = 1; sp0 < splits; sp0 += SPF) {
+    float tmp[SPF][VMAX];
+#pragma unroll
+    for (int u = 0; u < SPF; ++u)
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i)
+        tmp[u][i] = (!taken[i] && sp0 + u < splits) ? partial[(sp0 + u) * TE + (int64_t)t * E + i * G + g] : 0.f;
+#pragma unroll
+    for (int u = 0; u < SPF; ++u)
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i)
+        if (sp0 + u < splits) sum[i] += tmp[u][i];
+  }
+#pragma unroll
+  for (int i = 0; i < VMAX; ++i) {
+    val[i] = -INFINITY;
+    if (!taken[i]) {
+      const int e = i * G + g;
+      float s = sum[i];
+      if (bias) s += bias[(int64_t)t * bias_stride + e];
+      logits[(int64_t)t * E + e] = s;
+      s = s + 0.0f;                       // -0 -> +0: equal values compare equal either way
+      val[i] = (s == s) ? s : -INFINITY;  // NaN ranks as -inf
+    }
+  }
+
+  select_topk<G, VMAX>(val, taken, g, t, live, k, topk_ids, topk_w);
+}
+
+// Few experts: one workgroup of 256 threads per token computes the logits directly. Thread i
+// accumulates in fp32 the products of the 16-byte x chunks i, i + 256, ... with the matching fp32
+// router-weight slices of every expert (all loads of a chunk in flight at once; the router weight is
+// an L2 hit after the first token), a butterfly sums each expert over the wave, and wave 0 adds the
+// four wave sums in wave order (deterministic). Lane e (< E) of wave 0 then holds logit e for the
+// same selection as route_topk.
+template <typename TX, int EMAX>
+__global__ __launch_bounds__(256) void route_small_kernel(const TX* __restrict__ x, const float* __restrict__ w,
+                                                          const float* __restrict__ bias, int64_t bias_stride,
+                                                          int T, int H, int E, int k, float* __restrict__ logits,
+                                                          int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  constexpr int VN = Vec<TX>::N;  // x elements per 16-byte chunk
+  __shared__ float s_part[4][EMAX];
+  const int lane = lane_id(), wave = (int)(threadIdx.x >> 6);
+  const int t = blockIdx.x;
+  float acc[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) acc[e] = 0.f;
+  const TX* xr = x + (int64_t)t * H;
+#pragma unroll 2
+  for (int c = threadIdx.x; c * VN < H; c += 256) {
+    float xv[VN];
+    unpack(ld16(xr + c * VN), xv);
+    u32x4 wraw[EMAX][VN / 4];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+#pragma unroll
+      for (int q = 0; q < VN / 4; ++q)
+        if (e < E) wraw[e][q] = ld16(w + (int64_t)e * H + c * VN + q * 4);
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      if (e < E) {
+#pragma unroll
+        for (int q = 0; q < VN / 4; ++q) {
+          float wv[4];
+          unpack(wraw[e][q], wv);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[e] = fmaf(xv[q * 4 + r], wv[r], acc[e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) {
+    if (e < E) {
+      float v = acc[e];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      if (lane == 0) s_part[wave][e] = v;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float val[1];
+  bool taken[1];
+  taken[0] = lane >= E;
+  val[0] = -INFINITY;
+  if (!taken[0]) {
+    float s = ((s_part[0][lane] + s_part[1][lane]) + s_part[2][lane]) + s_part[3][lane];
+    if (bias) s += bias[(int64_t)t * bias_stride + lane];
+    logits[(int64_t)t * E + lane] = s;
+    s = s + 0.0f;                          // -0 -> +0
+    val[0] = (s == s) ? s : -INFINITY;     // NaN ranks as -inf
+  }
+  select_topk<64, 1>(val, taken, lane, t, true, k, topk_ids, topk_w);
+}
+
 }  // namespace
 
 // Host-side planning. Tile shape: fp32 activations use 64x64 fp32-MFMA tiles; bf16 activations use
@@ -386,11 +470,17 @@ RouteTiles route_tiles(int T, int xdt_bf16) {
   return RouteTiles{64, 64};
 }
 
+bool route_fused(int T, int E) { return E <= 16 && T <= ROUTE_FUSED_MAX_T; }
+
 int route_splits(int T, int H, int E, int xdt_bf16, int num_cus) {
+  if (route_fused(T, E)) return 1;
   const RouteTiles rt = route_tiles(T, xdt_bf16);
   const int tiles = ceil_div_host(T, rt.BM) * ceil_div_host(E, rt.BN);
   int s = ceil_div_host(2 * num_cus, tiles > 0 ? tiles : 1);
-  const int smax = H / 256 > 0 ? H / 256 : 1;
+  // at least 256 K per split, and few enough splits that the partial sums stay a small share of the
+  // traffic (the top-k kernel reads them all back)
+  int smax = H / 256 > 0 ? H / 256 : 1;
+  if (smax > ROUTE_MAX_SPLITS) smax = ROUTE_MAX_SPLITS;
   if (s > smax) s = smax;
   if (s < 1) s = 1;
   return s;
@@ -404,6 +494,22 @@ int route_k_split(int H, int splits) {
 hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, const float* bias,
                         int64_t bias_stride, int T, int H, int E, int k, float* logits, int* ids, float* wts,
                         float* partial, int splits, hipStream_t stream) {
+  if (route_fused(T, E)) {
+    const unsigned blocks = (unsigned)T;
+    const bool e8 = E <= 8;
+#define MOE_ROUTE_SMALL(TX, EM)                                                                         \
+  route_small_kernel<TX, EM><<<blocks, 256, 0, stream>>>(static_cast<const TX*>(x), w_router, bias,         \
+                                                         bias_stride, T, H, E, k, logits, ids, wts)
+    if (xdt_bf16) {
+      if (e8) MOE_ROUTE_SMALL(bf16_t, 8);
+      else MOE_ROUTE_SMALL(bf16_t, 16);
+    } else {
+      if (e8) MOE_ROUTE_SMALL(float, 8);
+      else MOE_ROUTE_SMALL(float, 16);
+    }
+#undef MOE_ROUTE_SMALL
+    return hipGetLastError();
+  }
   const int k_split = route_k_split(H, splits);
   const int nsplit = ceil_div_host(H, k_split);
   const RouteTiles rt = route_tiles(T, xdt_bf16);

@@ -105,9 +105,10 @@ int64_t moe_rows_max(int T, int k, int E, int C);
  *   w_router     [E, H] fp32 router weight
  *   logit_bias   NULL, or fp32 bias added to the logits; row t reads logit_bias[t*bias_row_stride + e]
  *                (stride 0: one [E] row for all tokens; stride E: a [T, E] matrix)
- *   logits       [T, E] fp32 output: sum_h x[t,h] * w_router[e,h] + bias, accumulated in fp32 (for
- *                bf16 x on bf16 MFMA, with w_router split exactly into three bf16 parts, so every
- *                product is the exact fp32 product)
+ *   logits       [T, E] fp32 output: sum_h x[t,h] * w_router[e,h] + bias, accumulated in fp32. Every
+ *                product is the exact fp32 product: with E <= 16 and T <= 4096 by fp32 FMAs, one
+ *                workgroup per token; otherwise on MFMA (bf16 x: bf16 MFMA with w_router split exactly
+ *                into three bf16 parts; fp32 x: fp32 MFMA)
  *   topk_ids     [T, k] int32 output: the k largest logits, descending, equal logits ordered by the
  *                lower expert id, -0 == +0 (slot 0 = best)
  *   topk_w       [T, k] fp32 output: softmax over the k selected logits (sums to 1)
@@ -120,7 +121,8 @@ int moe_route(const void* x, moe_dtype_t xdt, const float* w_router, const float
               float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of scratch `workspace` moe_route needs for (T, H, E, xdt): fp32 partial sums when the H
- * reduction is split across workgroups (0 when it is not; workspace may then be NULL). */
+ * reduction is split across workgroups (0 when it is not, e.g. for E <= 16 and T <= 4096; workspace
+ * may then be NULL). */
 size_t moe_route_workspace_bytes(int T, int H, int E, moe_dtype_t xdt);
 
 /* Bytes of scratch `workspace` moe_dispatch needs for (T, k, E). */

@@ -66,7 +66,10 @@ def test_workspace_sizes(lib):
         for xdt in (moe.MOE_BF16, moe.MOE_F32):
             n = moe.moe_route_workspace_bytes(T, H, E, xdt)
             assert n % (T * E * 4) == 0 and n != T * E * 4
-    assert moe.moe_route_workspace_bytes(128, 4096, 8, moe.MOE_BF16) > 0
+    # few experts and tokens: one fused kernel, no scratch; many experts: split-K partials
+    assert moe.moe_route_workspace_bytes(128, 4096, 8, moe.MOE_BF16) == 0
+    assert moe.moe_route_workspace_bytes(4096, 4096, 16, moe.MOE_F32) == 0
+    assert moe.moe_route_workspace_bytes(128, 7168, 384, moe.MOE_BF16) > 0
     assert moe.moe_route_workspace_bytes(128, 4096, 8, 9) == 0
 
 
@@ -90,7 +93,7 @@ def test_route_rejects_invalid_arguments(lib):
     assert _route(lib, ids=None) == MOE_ERR_INVALID
     assert _route(lib, bias=FAKE, stride=-1) == MOE_ERR_INVALID
     # needs scratch (split reduction) but none given
-    assert _route(lib, T=128, H=4096, E=8, ws=None, wsb=0) == MOE_ERR_INVALID
+    assert _route(lib, T=128, H=7168, E=384, k=8, ws=None, wsb=0) == MOE_ERR_INVALID
     # T == 0 is a no-op that succeeds without touching anything
     assert _route(lib, T=0, x=None, logits=None, ids=None, wts=None) == 0
 
