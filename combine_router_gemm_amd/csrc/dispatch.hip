@@ -31,11 +31,41 @@ namespace {
 
 constexpr int DR_THREADS = 256;
 constexpr int DR_WAVES = DR_THREADS / MOE_WAVE;
+static_assert(2 * DR_THREADS >= MOE_MAX_EXPERTS, "the one-block scan gives each thread two experts");
 
+// Exclusive scan of v over the DR_THREADS threads of the workgroup (thread order); *total gets the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int wbase = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < DR_WAVES; ++w) {
+    if (w < wave) wbase += s_wsum[w];
+    sum += s_wsum[w];
+  }
+  *total = sum;
+  return wbase + incl - v;
+}
+
+// SCAN (one block, T <= DISPATCH_TB): the block is the whole batch, so its per-expert bases are 0 and
+// the block also writes count / kept / overflow and the expert offsets, in place of dispatch_scan.
+template <bool SCAN>
 __global__ __launch_bounds__(DR_THREADS) void dispatch_rank_kernel(const int* __restrict__ ids, int T, int k,
                                                                   int E, int* __restrict__ blk_count,
-                                                                  int* __restrict__ pair_local) {
+                                                                  int* __restrict__ pair_local, int C,
+                                                                  int* __restrict__ count, int* __restrict__ kept,
+                                                                  int* __restrict__ overflow,
+                                                                  int* __restrict__ offset) {
   __shared__ int cnt[DR_WAVES][MOE_MAX_EXPERTS];
+  __shared__ int s_tot[SCAN ? MOE_MAX_EXPERTS : 1];
+  __shared__ int s_wsum[DR_WAVES];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -91,9 +121,35 @@ __global__ __launch_bounds__(DR_THREADS) void dispatch_rank_kernel(const int* __
       cnt[w][e] = acc;
       acc += c;
     }
-    blk_count[(int64_t)blockIdx.x * E + e] = acc;
+    if (SCAN) {
+      blk_count[e] = 0;
+      s_tot[e] = acc;
+    } else {
+      blk_count[(int64_t)blockIdx.x * E + e] = acc;
+    }
   }
   __syncthreads();
+  if (SCAN) {
+    // thread i owns experts 2i and 2i + 1 (E <= 2 * DR_THREADS)
+    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
+    const int k0 = e0 < E ? min(s_tot[e0], C) : 0;
+    const int k1 = e1 < E ? min(s_tot[e1], C) : 0;
+    int total = 0;
+    const int excl = block_exclusive_scan(k0 + k1, s_wsum, &total);
+    if (e0 < E) {
+      count[e0] = s_tot[e0];
+      kept[e0] = k0;
+      overflow[e0] = s_tot[e0] - k0;
+      offset[e0] = excl;
+    }
+    if (e1 < E) {
+      count[e1] = s_tot[e1];
+      kept[e1] = k1;
+      overflow[e1] = s_tot[e1] - k1;
+      offset[e1] = excl + k0;
+    }
+    if (threadIdx.x == 0) offset[E] = total;
+  }
 #pragma unroll
   for (int c = 0; c < MOE_MAX_TOPK; ++c) {
     if (c < k) {
@@ -219,10 +275,18 @@ int dispatch_num_blocks(int T) { return ceil_div_host(T, DISPATCH_TB); }
 hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const moe_layout_t& L, void* send_buf,
                            int* blk_count, int* pair_local, hipStream_t stream) {
   const int nblk = dispatch_num_blocks(L.T);
-  if (nblk > 0) dispatch_rank_kernel<<<nblk, DR_THREADS, 0, stream>>>(ids, L.T, L.k, L.E, blk_count, pair_local);
-  // with no tokens the scan still writes zero counts and offsets
-  dispatch_scan_kernel<<<1, DS_THREADS, 0, stream>>>(blk_count, nblk, L.E, L.C, L.expert_count, L.expert_kept,
-                                                     L.expert_overflow, L.expert_offset);
+  if (nblk == 1) {  // one block: it scans too
+    dispatch_rank_kernel<true><<<1, DR_THREADS, 0, stream>>>(ids, L.T, L.k, L.E, blk_count, pair_local, L.C,
+                                                             L.expert_count, L.expert_kept, L.expert_overflow,
+                                                             L.expert_offset);
+  } else {
+    if (nblk > 0)
+      dispatch_rank_kernel<false><<<nblk, DR_THREADS, 0, stream>>>(ids, L.T, L.k, L.E, blk_count, pair_local, L.C,
+                                                                   nullptr, nullptr, nullptr, nullptr);
+    // with no tokens the scan still writes zero counts and offsets
+    dispatch_scan_kernel<<<1, DS_THREADS, 0, stream>>>(blk_count, nblk, L.E, L.C, L.expert_count, L.expert_kept,
+                                                       L.expert_overflow, L.expert_offset);
+  }
   if (L.T == 0) return hipGetLastError();
   // slices per lane in flight: enough for the whole row in one pass up to 1024 slices (bf16 H <= 8192)
   const int nvec = L.H / (xdt_bf16 ? 8 : 4);

@@ -251,6 +251,8 @@ EDGE = [
     ("dl256_ragged_R2", 2600, 320, 4, 2, 192, 2, 1100, "bf16", "zipf"),
     # 64-row weight-streaming tiles (capacity 75 rows per expert on average), hot experts over 64 rows
     ("dec64_multi_mtile", 300, 128, 8, 2, 96, 1, 100, "bf16", "zipf"),
+    # one counting block (T <= 256) scans all 512 experts itself
+    ("E512_one_block", 200, 64, 512, 8, 32, 8, 4, "bf16", "zipf"),
 ]
 
 
