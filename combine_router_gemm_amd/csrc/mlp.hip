@@ -16,15 +16,20 @@
 //   mlp_gemm      persistent MFMA GEMM, C[p, n] = sum_k A[p, k] * B[n, k] ("NT": both operands are
 //                 K-contiguous, the nn.Linear [out, in] layout). Tiles are visited local expert major,
 //                 then N tile, then M tile, so workgroups running side by side share a weight slice;
-//                 the workgroup -> tile map groups consecutive tiles on one XCD (workgroups are dealt
+//                 the tile list is cut into 8 equal contiguous ranges, one per XCD (workgroups are dealt
 //                 to the 8 XCDs round robin, and each XCD has its own L2).
 //                 Gate/up pass: A rows gathered through perm from the send buffer, B = the gate and the
 //                 up rows of the same output columns, epilogue h = silu(g) * u (fp32) stored as xdt.
 //                 Down pass: A = h in plan order, epilogue stores to out_buf[perm[p]] as xdt.
-//   Operands are staged global -> registers -> LDS with several stages of global loads in flight and
-//   two LDS stages (one barrier per stage). Compute-bound bf16 tiles use v_mfma_f32_32x32x16_bf16,
-//   weight-streaming bf16 tiles v_mfma_f32_16x16x32_bf16, fp32 v_mfma_f32_16x16x4_f32; all accumulate
-//   in fp32.
+//   Two kernel families share that structure:
+//     mlp_gemm_kernel     operands staged global -> registers -> LDS (buffer loads, several register
+//                         stages in flight). Few rows per expert (weight streaming, 32- or 64-row tiles
+//                         on v_mfma_f32_16x16x32_bf16), fp32 (v_mfma_f32_16x16x4_f32), and the bf16
+//                         fallback for shapes the other family does not take.
+//     mlp_gemm_dl_kernel  many rows per expert: operands go global -> LDS directly (buffer loads with
+//                         the LDS bit), NS LDS stages in flight, 128- or 256-row tiles on
+//                         v_mfma_f32_32x32x16_bf16, epilogue staged through LDS.
+//   All accumulate in fp32.
 #include "common.h"
 #include "kernels.h"
 #include "mfma.h"
@@ -422,6 +427,7 @@ void mlp_gemm_kernel(GemmArgs args) {
 // global chunk each lane fetches, so the 32-row MFMA fragment reads hit distinct LDS banks. Rows past
 // the tile are fetched at an offset beyond the buffer's record count, which the hardware returns as
 // zeros. Requires K % 64 == 0 and operand buffers below 2 GiB (the host falls back otherwise).
+
 // chunk swizzle of row r for CPR 16-byte chunks per row (CPR = 8 for 128-byte rows, 4 for 64-byte rows);
 // SWZ 1 spreads 16 consecutive rows over distinct (row parity, chunk) bank slots
 template <int SWZ, int CPR>
@@ -435,7 +441,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool GATED, int NS, int SWZ, bool SPREAD, bool FENCE>
+template <int BM, int BN, int BK, int WM, int WN, bool GATED, int NS, int SWZ, bool SPREAD>
 __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args, int a_bytes) {
   using Op = Op32;
   static_assert(BK == 32 || BK == 64, "32- or 64-deep stages");
@@ -595,8 +601,6 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[ks & 1][i], bfg[ks & 1][j]);
-        // keep the scheduler from hoisting later steps' fragment reads (register pressure)
-        if (FENCE) __builtin_amdgcn_sched_barrier(0);
       }
     };
 
@@ -736,9 +740,6 @@ void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
 #ifndef MOE_DL_SPREAD
 #define MOE_DL_SPREAD true
 #endif
-#ifndef MOE_DL_FENCE
-#define MOE_DL_FENCE false
-#endif
 // 256-row tile
 #ifndef MOE_DLT_BN
 #define MOE_DLT_BN 256
@@ -815,10 +816,10 @@ template <int BM, int BN, int WM, int WN, int NS, bool SPREAD>
 void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
                int64_t h_bytes, int num_cus, hipStream_t stream) {
   const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, BN / 2), num_cus, MOE_DL_WPC);
-  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, true, NS, MOE_DL_SWZ, SPREAD, MOE_DL_FENCE><<<g1, WM * WN * 64, 0, stream>>>(
+  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, true, NS, MOE_DL_SWZ, SPREAD><<<g1, WM * WN * 64, 0, stream>>>(
       gu, (int)send_bytes);
   const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, BN), num_cus, MOE_DL_WPC);
-  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, false, NS, MOE_DL_SWZ, SPREAD, MOE_DL_FENCE><<<g2, WM * WN * 64, 0, stream>>>(
+  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, false, NS, MOE_DL_SWZ, SPREAD><<<g2, WM * WN * 64, 0, stream>>>(
       dn, (int)h_bytes);
 }
 
