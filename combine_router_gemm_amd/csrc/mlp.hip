@@ -138,6 +138,9 @@ __global__ __launch_bounds__(PLAN_THREADS) void mlp_plan_kernel(const int* __res
 // ------------------------------------------------------------------------------------------------
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
+#ifndef MOE_K_ROTATE
+#define MOE_K_ROTATE 1
+#endif
 #ifndef MOE_GEMM_MIN_WAVES
 #define MOE_GEMM_MIN_WAVES 1
 #endif
@@ -158,7 +161,18 @@ struct GemmArgs {
   int El;
   int a_bytes;          // bytes of A (rows_max x lda elements) when it fits 31-bit buffer offsets, else 0
   int w_bytes;          // bytes of one expert's weights (w_stride elements), same rule
+  int k_rotate;         // start each tile's K loop at a tile-dependent stage (see k_rotation)
 };
+
+// Weight rows whose pitch is a multiple of 8 KB put the same K slice of every row of a tile on the same
+// HBM channels while all tiles walk K in step: a read probe of the weight-streaming tile pattern
+// measured 5.4 TB/s at an 8192-byte pitch against 6.0 TB/s at 8448 bytes, and rotating each tile's
+// starting stage recovers it. Tiles that share weights (the M tiles of one expert and N tile) get the
+// same rotation, so they keep sharing them through L2.
+__device__ __forceinline__ int k_rotation(int on, int l, int n_tiles, int nt, int nk) {
+  return on ? (int)(((int64_t)l * n_tiles + nt) * 7 % nk) : 0;
+}
+inline int k_rotate_for(int K, int elem_bytes) { return MOE_K_ROTATE && ((int64_t)K * elem_bytes) % 8192 == 0; }
 
 // BM x BN tile, BK-deep LDS stages, WM x WN waves, MFMA op Op. GATED: the B tile holds BN/2 gate rows
 // then the BN/2 up rows of the same output columns, and each wave owns matching gate and up
@@ -199,12 +213,20 @@ void mlp_gemm_kernel(GemmArgs args) {
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, BUF ? args.a_bytes : 0, 0x00020000);
   const int El = args.El;
-  const int* row_start = args.plan + 2;
-  const int* tile_start = args.plan + 3 + El;
   const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
   const int total = args.plan[0] * n_tiles;
 
   const int tid = threadIdx.x;
+  // the plan's row and tile starts, copied to LDS once: every tile start then resolves its expert
+  // with LDS reads instead of a chain of dependent global loads
+  __shared__ int s_plan[2 * (MOE_MAX_EXPERTS + 1)];
+  int* row_start = s_plan;
+  int* tile_start = s_plan + MOE_MAX_EXPERTS + 1;
+  for (int i = tid; i <= El; i += NTH) {
+    row_start[i] = args.plan[2 + i];
+    tile_start[i] = args.plan[3 + El + i];
+  }
+  __syncthreads();
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -296,10 +318,13 @@ void mlp_gemm_kernel(GemmArgs args) {
     // RS register stages of global loads in flight: stage s + RS is requested before the MFMAs of
     // stage s run, and stage s + 1 moves from registers to LDS after them (one barrier per stage).
     const int nk = (args.K + BK - 1) / BK;
+    const int rot = k_rotation(args.k_rotate, l, n_tiles, nt, nk);
+    // stage st of the loop reads K slice (st + rot) mod nk
+    auto kslice = [&](int st) { return (st + rot < nk ? st + rot : st + rot - nk) * BK; };
     u32x4 ra[RS][A_VEC], rb[RS][B_VEC];
     const u32x4 zero = {0u, 0u, 0u, 0u};
     auto load_stage = [&](int st, u32x4 (&xa)[A_VEC], u32x4 (&xb)[B_VEC]) {
-      const int k0 = st * BK;
+      const int k0 = kslice(st);
 #pragma unroll
       for (int i = 0; i < A_VEC; ++i) {
         const int col = min(k0 + a_lds[i] % LDR, args.K - VN);
@@ -325,7 +350,7 @@ void mlp_gemm_kernel(GemmArgs args) {
       }
     };
     auto store_stage = [&](int st, int buf, const u32x4 (&xa)[A_VEC], const u32x4 (&xb)[B_VEC]) {
-      const int k0 = st * BK;
+      const int k0 = kslice(st);
 #pragma unroll
       for (int i = 0; i < A_VEC; ++i) st16(&As[buf][a_lds[i]], (a_ok[i] && k0 + a_lds[i] % LDR < args.K) ? xa[i] : zero);
 #pragma unroll
@@ -881,6 +906,7 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   gu.El = El;
   gu.a_bytes = buffer_bytes(rows_max * H * (xdt_bf16 ? 2 : 4));
   gu.w_bytes = buffer_bytes(gu.w_stride * (xdt_bf16 ? 2 : 4));
+  gu.k_rotate = k_rotate_for(H, xdt_bf16 ? 2 : 4);
 
   GemmArgs dn{};
   dn.A = hbuf;
@@ -898,6 +924,7 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   dn.El = El;
   dn.a_bytes = buffer_bytes(rows_max * F * (xdt_bf16 ? 2 : 4));
   dn.w_bytes = buffer_bytes(dn.w_stride * (xdt_bf16 ? 2 : 4));
+  dn.k_rotate = k_rotate_for(F, xdt_bf16 ? 2 : 4);
 
   switch (tiles.variant) {
     case 3:
