@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, i
     sum[i] = taken[i] ? 0.f : partial[(int64_t)t * E + e];
   }
   // the remaining K-split partials, SPF splits of loads in flight at a time, added in split order
-  constexpr int SPF = 8;
+  constexpr int SPF = 4;
   const int64_t TE = (int64_t)T * E;
   for (int sp0 = 1; sp0 < splits; sp0 += SPF) {
     float tmp[SPF][VMAX];
