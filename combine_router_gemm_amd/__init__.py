@@ -17,20 +17,21 @@ from typing import Optional
 
 import torch
 
-__all__ = ["MOE_F32", "MOE_BF16", "MoeError", "Layout", "library_path", "load_library", "moe_route",
-           "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_rows_max", "moe_route_workspace_bytes",
-           "moe_dispatch_workspace_bytes", "moe_expert_mlp_workspace_bytes", "moe_status_string",
-           "EXPORTED_SYMBOLS"]
+__all__ = ["MOE_F32", "MOE_BF16", "MOE_FP8_BLOCK", "MoeError", "Layout", "library_path", "load_library",
+           "moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_dispatch_fp8", "moe_expert_mlp_fp8",
+           "moe_rows_max", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
+           "moe_expert_mlp_workspace_bytes", "moe_status_string", "EXPORTED_SYMBOLS"]
 
 MOE_F32 = 0
 MOE_BF16 = 1
+MOE_FP8_BLOCK = 128  # hidden elements per fp8 block scale
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmoe_gfx950.so"
 
 EXPORTED_SYMBOLS = ("moe_status_string", "moe_rows_max", "moe_route_workspace_bytes", "moe_route",
                     "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_expert_mlp_workspace_bytes",
-                    "moe_expert_mlp", "moe_combine")
+                    "moe_expert_mlp", "moe_combine", "moe_dispatch_fp8", "moe_expert_mlp_fp8")
 
 
 class MoeError(RuntimeError):
@@ -80,6 +81,10 @@ def load_library():
     lib.moe_expert_mlp.restype = i32
     lib.moe_combine.argtypes = [vp, i32, ctypes.POINTER(_CLayout), vp, vp, vp]
     lib.moe_combine.restype = i32
+    lib.moe_dispatch_fp8.argtypes = [vp, i32, vp, ctypes.POINTER(_CLayout), vp, vp, vp, sz, vp]
+    lib.moe_dispatch_fp8.restype = i32
+    lib.moe_expert_mlp_fp8.argtypes = [vp, vp, ctypes.POINTER(_CLayout), vp, vp, i32, vp, vp, sz, vp]
+    lib.moe_expert_mlp_fp8.restype = i32
     _lib = lib
     return lib
 
@@ -270,3 +275,43 @@ def moe_combine(out_buf: torch.Tensor, layout: Layout, topk_w: torch.Tensor, y: 
         _ptr(out_buf, "out_buf"), _dtype_code(y), ctypes.byref(cl),
         _ptr(topk_w, "topk_w", torch.float32, (L.T, L.k), dev), _ptr(y, "y"), _stream(stream))
     _check(st, "moe_combine")
+
+
+def moe_dispatch_fp8(x: torch.Tensor, topk_ids: torch.Tensor, layout: Layout, send_q: torch.Tensor,
+                     send_scale: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """moe_dispatch with fp8 block-scaled send rows: E4M3 codes (uint8) and one power-of-two fp32 scale
+    per 128 hidden elements. x must be bf16."""
+    dev = x.device
+    L = layout
+    _ptr(x, "x", torch.bfloat16, (L.T, L.H), dev)
+    _ptr(send_q, "send_q", torch.uint8, (L.rows_max, L.H), dev)
+    _ptr(send_scale, "send_scale", torch.float32, (L.rows_max, L.H // MOE_FP8_BLOCK), dev)
+    ws = _workspace(moe_dispatch_workspace_bytes(L.T, L.k, L.E), workspace, dev)
+    cl = L.c_struct()
+    st = load_library().moe_dispatch_fp8(
+        _ptr(x, "x"), MOE_BF16, _ptr(topk_ids, "topk_ids", torch.int32, (L.T, L.k), dev), ctypes.byref(cl),
+        _ptr(send_q, "send_q"), _ptr(send_scale, "send_scale"), _ptr(ws, "workspace"),
+        0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "moe_dispatch_fp8")
+
+
+def moe_expert_mlp_fp8(send_q: torch.Tensor, send_scale: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor,
+                       w_down: torch.Tensor, out_buf: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """Expert SwiGLU MLP on fp8 block-scaled rows (decoded to bf16 in the GEMM); bf16 weights and output."""
+    dev = send_q.device
+    L = layout
+    El = L.E // L.R
+    F = w_gate_up.shape[1] // 2
+    _ptr(send_q, "send_q", torch.uint8, (L.rows_max, L.H), dev)
+    _ptr(send_scale, "send_scale", torch.float32, (L.rows_max, L.H // MOE_FP8_BLOCK), dev)
+    _ptr(w_gate_up, "w_gate_up", torch.bfloat16, (El, 2 * F, L.H), dev)
+    _ptr(w_down, "w_down", torch.bfloat16, (El, L.H, F), dev)
+    _ptr(out_buf, "out_buf", torch.bfloat16, (L.rows_max, L.H), dev)
+    ws = _workspace(moe_expert_mlp_workspace_bytes(L.T, L.k, L.E, L.R, L.C, F, MOE_BF16), workspace, dev)
+    cl = L.c_struct()
+    st = load_library().moe_expert_mlp_fp8(
+        _ptr(send_q, "send_q"), _ptr(send_scale, "send_scale"), ctypes.byref(cl), _ptr(w_gate_up, "w_gate_up"),
+        _ptr(w_down, "w_down"), F, _ptr(out_buf, "out_buf"), _ptr(ws, "workspace"), 0 if ws is None else ws.numel(),
+        _stream(stream))
+    _check(st, "moe_expert_mlp_fp8")

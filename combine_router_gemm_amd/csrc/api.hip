@@ -122,9 +122,12 @@ size_t moe_expert_mlp_workspace_bytes(int T, int k, int E, int R, int C, int F, 
          moe::align256((size_t)rows * (size_t)F * esz);
 }
 
-int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* layout, const void* w_gate_up,
-                   const void* w_down, int F, void* out_buf, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+namespace {
+// Shared by moe_expert_mlp and moe_expert_mlp_fp8: validation, workspace carving, launch. a_scale !=
+// nullptr means send_buf holds E4M3 codes with these block scales.
+int expert_mlp(const void* send_buf, const float* a_scale, moe_dtype_t xdt, const moe_layout_t* layout,
+               const void* w_gate_up, const void* w_down, int F, void* out_buf, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
   if (!valid_dtype(xdt)) return MOE_ERR_UNSUPPORTED;
   const int st = check_layout(layout);
   if (st != MOE_OK) return st;
@@ -144,9 +147,59 @@ int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* la
   int* perm = reinterpret_cast<int*>(ws);
   ws += moe::align256((size_t)rows * sizeof(int));
   void* hbuf = ws;
-  const moe::MlpTiles tiles = moe::mlp_pick_tiles(rows, El, L.H, F, xdt == MOE_BF16);
+  const moe::MlpTiles tiles = moe::mlp_pick_tiles(rows, El, L.H, F, xdt == MOE_BF16, a_scale != nullptr);
   return hip_status(moe::launch_expert_mlp(send_buf, xdt == MOE_BF16, L, w_gate_up, w_down, F, out_buf, plan, perm,
-                                           hbuf, tiles, device_cus(), stream));
+                                           hbuf, tiles, device_cus(), stream, a_scale));
+}
+
+// fp8 rows and weights must fit 31-bit buffer offsets (the fp8 GEMM path reads them with buffer loads)
+bool fp8_fits(int64_t rows, int H, int F) {
+  const int64_t lim = 0x7ffffff0ll - 256;
+  return rows * (int64_t)H < lim && rows * (int64_t)(H / MOE_FP8_BLOCK) * 4 < lim && rows * (int64_t)F * 2 < lim &&
+         (int64_t)2 * F * H * 2 < lim && (int64_t)H * F * 2 < lim;
+}
+}  // namespace
+
+int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* layout, const void* w_gate_up,
+                   const void* w_down, int F, void* out_buf, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  return expert_mlp(send_buf, nullptr, xdt, layout, w_gate_up, w_down, F, out_buf, workspace, workspace_bytes,
+                    stream);
+}
+
+int moe_dispatch_fp8(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const moe_layout_t* layout,
+                     uint8_t* send_q, float* send_scale, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  if (xdt != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int st = check_layout(layout);
+  if (st != MOE_OK) return st;
+  const moe_layout_t& L = *layout;
+  if (L.H % MOE_FP8_BLOCK != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
+  if (L.T > 0 && (!x || !topk_ids)) return MOE_ERR_INVALID;
+  if (rows > 0 && (!send_q || !send_scale)) return MOE_ERR_INVALID;
+  const size_t need = moe_dispatch_workspace_bytes(L.T, L.k, L.E);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_INVALID;
+  char* ws = static_cast<char*>(workspace);
+  int* blk_count = reinterpret_cast<int*>(ws);
+  int* pair_local =
+      reinterpret_cast<int*>(ws + moe::align256((size_t)moe::dispatch_num_blocks(L.T) * L.E * sizeof(int)));
+  return hip_status(moe::launch_dispatch_fp8(x, topk_ids, L, send_q, send_scale, blk_count, pair_local, stream));
+}
+
+int moe_expert_mlp_fp8(const uint8_t* send_q, const float* send_scale, const moe_layout_t* layout,
+                       const void* w_gate_up, const void* w_down, int F, void* out_buf, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_layout(layout);
+  if (st != MOE_OK) return st;
+  const moe_layout_t& L = *layout;
+  if (L.H % MOE_FP8_BLOCK != 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
+  if (rows > 0 && !send_scale) return MOE_ERR_INVALID;
+  if (F >= 1 && F % 8 == 0 && !fp8_fits(rows, L.H, F)) return MOE_ERR_UNSUPPORTED;
+  // with no rows there is nothing to decode: the bf16 path launches only the (empty) plan
+  return expert_mlp(send_q, rows > 0 ? send_scale : nullptr, MOE_BF16, layout, w_gate_up, w_down, F, out_buf,
+                    workspace, workspace_bytes, stream);
 }
 
 int moe_combine(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout, const float* topk_w, void* y,

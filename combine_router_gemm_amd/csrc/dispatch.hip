@@ -212,14 +212,11 @@ __global__ __launch_bounds__(DS_THREADS) void dispatch_scan_kernel(int* __restri
 // stores. A token whose pairs were all dropped is not read.
 constexpr int SCATTER_WAVES = 4;
 
-template <typename T, int VPL>
-__global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_kernel(
-    const T* __restrict__ x, const int* __restrict__ ids, int T_, int H, int k, int E, int C,
-    const int* __restrict__ blk_base, const int* __restrict__ pair_local, const int* __restrict__ offset,
-    int* __restrict__ row_token, int* __restrict__ row_slot, int* __restrict__ pair_row, T* __restrict__ send_buf) {
-  const int lane = lane_id();
-  const int t = blockIdx.x * SCATTER_WAVES + (int)(threadIdx.x >> 6);
-  if (t >= T_) return;
+// Row of pair (t, lane) for lanes < k (-1 if dropped or not a pair), with the layout entries written.
+__device__ __forceinline__ int resolve_pair_row(int t, int lane, const int* __restrict__ ids, int k, int E, int C,
+                                                const int* __restrict__ blk_base, const int* __restrict__ pair_local,
+                                                const int* __restrict__ offset, int* __restrict__ row_token,
+                                                int* __restrict__ row_slot, int* __restrict__ pair_row) {
   int row = -1;
   if (lane < k) {
     const int64_t p = (int64_t)t * k + lane;
@@ -235,6 +232,18 @@ __global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_kernel(
       row_slot[row] = lane;
     }
   }
+  return row;
+}
+
+template <typename T, int VPL>
+__global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_kernel(
+    const T* __restrict__ x, const int* __restrict__ ids, int T_, int H, int k, int E, int C,
+    const int* __restrict__ blk_base, const int* __restrict__ pair_local, const int* __restrict__ offset,
+    int* __restrict__ row_token, int* __restrict__ row_slot, int* __restrict__ pair_row, T* __restrict__ send_buf) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * SCATTER_WAVES + (int)(threadIdx.x >> 6);
+  if (t >= T_) return;
+  const int row = resolve_pair_row(t, lane, ids, k, E, C, blk_base, pair_local, offset, row_token, row_slot, pair_row);
   uint64_t kept = __ballot(row >= 0);  // only lanes < k can hold a row
   if (kept == 0) return;               // every pair of this token was dropped: nothing to copy
   constexpr int VN = Vec<T>::N;
@@ -268,12 +277,106 @@ void launch_scatter_t(const void* x, const int* ids, const moe_layout_t& L, void
       L.row_slot, L.pair_row, static_cast<T*>(send_buf));
 }
 
+// ---- fp8 block-scaled rows ----
+// OCP E4M3 code of y (|y| <= 448 after clamping), nearest value with ties to the even mantissa, sign
+// kept. Below 2^-6 the quantum is 2^-9, so the code is y * 2^9 rounded (8 there is the smallest normal,
+// whose code is 8 too); above, the fp32 fraction is rounded to 3 bits, carrying into the exponent.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = __float_as_uint(y) >> 31;
+  const float a = fminf(fabsf(y), 448.0f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)rintf(a * 512.0f);
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    b &= ~0xFFFFFu;
+    const int e = (int)(b >> 23) - 127;  // -6 .. 8
+    code = ((uint32_t)(e + 7) << 3) | ((b >> 20) & 7u);
+  }
+  return code | (sign << 7);
+}
+
+// Exponent E of the block scale: the smallest integer with amax / 2^E <= 448. With amax = f * 2^fe,
+// f in [0.5, 1), amax / 448 = (f / 0.875) * 2^(fe - 9), and f / 0.875 is in (0.5, 1] iff f <= 0.875.
+__device__ __forceinline__ int e4m3_block_exp(float amax) {
+  if (amax == 0.0f) return 0;
+  int fe;
+  const float f = frexpf(amax, &fe);
+  return fe - 9 + (f > 0.875f ? 1 : 0);
+}
+
+// One wave per token (as dispatch_scatter). A pass covers 64 * VPL 16-byte chunks of 8 bf16 values; a
+// 128-element block is 16 chunks held by 16 consecutive lanes, which find the block maximum with
+// shuffles. Each lane stores its 8 codes (8 bytes) to every kept row; the block's first lane stores
+// the scale.
+template <int VPL>
+__global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_fp8_kernel(
+    const bf16_t* __restrict__ x, const int* __restrict__ ids, int T_, int H, int k, int E, int C,
+    const int* __restrict__ blk_base, const int* __restrict__ pair_local, const int* __restrict__ offset,
+    int* __restrict__ row_token, int* __restrict__ row_slot, int* __restrict__ pair_row, uint8_t* __restrict__ send_q,
+    float* __restrict__ send_scale) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * SCATTER_WAVES + (int)(threadIdx.x >> 6);
+  if (t >= T_) return;
+  const int row = resolve_pair_row(t, lane, ids, k, E, C, blk_base, pair_local, offset, row_token, row_slot, pair_row);
+  const uint64_t kept = __ballot(row >= 0);
+  if (kept == 0) return;
+  const int nvec = H / 8;  // H % 128 == 0, so every pass holds whole blocks
+  const int nblk = H / 128;
+  const bf16_t* src = x + (int64_t)t * H;
+  for (int base = 0; base < nvec; base += 64 * VPL) {
+    u32x4 val[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int v = base + lane + i * 64;
+      if (v < nvec) val[i] = ld16(src + (int64_t)v * 8);
+    }
+    u32x2 q[VPL];
+    float sc[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int v = base + lane + i * 64;
+      float f[8];
+      unpack(v < nvec ? val[i] : u32x4{0u, 0u, 0u, 0u}, f);
+      float am = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) am = fmaxf(am, fabsf(f[j]));
+      // block maximum over the 16 lanes of this block (lane groups of 16 are aligned: base % 64 == 0)
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
+      const int E8 = e4m3_block_exp(am);
+      sc[i] = ldexpf(1.0f, E8);
+      uint32_t c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = e4m3_code(ldexpf(f[j], -E8));  // exact scaling by 2^-E
+      q[i].x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+      q[i].y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    }
+    for (uint64_t m = kept; m; m &= m - 1) {
+      const int j = __builtin_ctzll(m);
+      const int r = __shfl(row, j, 64);
+      uint8_t* dq = send_q + (int64_t)r * H;
+      float* ds = send_scale + (int64_t)r * nblk;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int v = base + lane + i * 64;
+        if (v < nvec) {
+          __builtin_nontemporal_store(q[i], reinterpret_cast<u32x2*>(dq + (int64_t)v * 8));
+          if ((lane & 15) == 0) ds[v >> 4] = sc[i];
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 int dispatch_num_blocks(int T) { return ceil_div_host(T, DISPATCH_TB); }
 
-hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const moe_layout_t& L, void* send_buf,
-                           int* blk_count, int* pair_local, hipStream_t stream) {
+// histogram + scan: the per-block ranks, counts, kept / overflow and offsets
+static hipError_t launch_counts(const int* ids, const moe_layout_t& L, int* blk_count, int* pair_local,
+                                hipStream_t stream) {
   const int nblk = dispatch_num_blocks(L.T);
   if (nblk == 1) {  // one block: it scans too
     dispatch_rank_kernel<true><<<1, DR_THREADS, 0, stream>>>(ids, L.T, L.k, L.E, blk_count, pair_local, L.C,
@@ -287,7 +390,13 @@ hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const mo
     dispatch_scan_kernel<<<1, DS_THREADS, 0, stream>>>(blk_count, nblk, L.E, L.C, L.expert_count, L.expert_kept,
                                                        L.expert_overflow, L.expert_offset);
   }
-  if (L.T == 0) return hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const moe_layout_t& L, void* send_buf,
+                           int* blk_count, int* pair_local, hipStream_t stream) {
+  const hipError_t st = launch_counts(ids, L, blk_count, pair_local, stream);
+  if (st != hipSuccess || L.T == 0) return st;
   // slices per lane in flight: enough for the whole row in one pass up to 1024 slices (bf16 H <= 8192)
   const int nvec = L.H / (xdt_bf16 ? 8 : 4);
   const int vpl = nvec > 256 ? 16 : (nvec > 64 ? 4 : 1);
@@ -300,6 +409,23 @@ hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const mo
     else if (vpl == 4) launch_scatter_t<float, 4>(x, ids, L, send_buf, blk_count, pair_local, stream);
     else launch_scatter_t<float, 1>(x, ids, L, send_buf, blk_count, pair_local, stream);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_fp8(const void* x, const int* ids, const moe_layout_t& L, uint8_t* send_q,
+                               float* send_scale, int* blk_count, int* pair_local, hipStream_t stream) {
+  const hipError_t st = launch_counts(ids, L, blk_count, pair_local, stream);
+  if (st != hipSuccess || L.T == 0) return st;
+  const int nvec = L.H / 8;
+  const unsigned blocks = (unsigned)ceil_div_host(L.T, SCATTER_WAVES);
+#define MOE_SCATTER_FP8(VPL)                                                                                 \
+  dispatch_scatter_fp8_kernel<VPL><<<blocks, SCATTER_WAVES * 64, 0, stream>>>(                              \
+      static_cast<const bf16_t*>(x), ids, L.T, L.H, L.k, L.E, L.C, blk_count, pair_local, L.expert_offset,       \
+      L.row_token, L.row_slot, L.pair_row, send_q, send_scale)
+  if (nvec > 256) MOE_SCATTER_FP8(16);
+  else if (nvec > 64) MOE_SCATTER_FP8(4);
+  else MOE_SCATTER_FP8(1);
+#undef MOE_SCATTER_FP8
   return hipGetLastError();
 }
 

@@ -29,17 +29,20 @@ constexpr int DISPATCH_TB = 256;  // tokens per counting block
 int dispatch_num_blocks(int T);
 hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const moe_layout_t& L, void* send_buf,
                            int* blk_count, int* pair_local, hipStream_t stream);
+hipError_t launch_dispatch_fp8(const void* x, const int* ids, const moe_layout_t& L, uint8_t* send_q,
+                               float* send_scale, int* blk_count, int* pair_local, hipStream_t stream);
 
 // ---- expert MLP ----
 struct MlpTiles {
   int BM;       // rows per tile (shared by both GEMMs; the plan is built for it)
   int variant;  // kernel family, see mlp.hip
 };
-MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16);
+MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16, int fp8_a);
 size_t mlp_plan_ints(int El);
+// a_scale != nullptr: send_buf holds E4M3 codes with these block scales (bf16 GEMM on the decoded rows)
 hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
                              const void* w_down, int F, void* out_buf, int* plan, int* perm, void* hbuf,
-                             const MlpTiles& tiles, int num_cus, hipStream_t stream);
+                             const MlpTiles& tiles, int num_cus, hipStream_t stream, const float* a_scale);
 
 // ---- combine ----
 hipError_t launch_combine(const void* out_buf, int xdt_bf16, const moe_layout_t& L, const float* topk_w, void* y,

@@ -162,7 +162,30 @@ struct GemmArgs {
   int a_bytes;          // bytes of A (rows_max x lda elements) when it fits 31-bit buffer offsets, else 0
   int w_bytes;          // bytes of one expert's weights (w_stride elements), same rule
   int k_rotate;         // start each tile's K loop at a tile-dependent stage (see k_rotation)
+  const float* a_scale; // fp8 A only: [rows, lda / 128] power-of-two block scales
+  int s_bytes;          // bytes of a_scale
 };
+
+// Value of an OCP E4M3 code (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
+// subnormal, 2^-6 * m/8). The codes the fp8 dispatch writes are never NaN.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Eight E4M3 codes (q.x, q.y, little-endian bytes) times their block scale (q.z, a power of two) as
+// eight bf16 values: code * scale has at most 4 significant bits, so the bf16 rounding is exact.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x4 q) {
+  const float sc = __uint_as_float(q.z);
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = e4m3_value((q.x >> (8 * j)) & 0xFFu) * sc;
+    f[4 + j] = e4m3_value((q.y >> (8 * j)) & 0xFFu) * sc;
+  }
+  return pack(f);
+}
 
 // Weight rows whose pitch is a multiple of 8 KB put the same K slice of every row of a tile on the same
 // HBM channels while all tiles walk K in step: a read probe of the weight-streaming tile pattern
@@ -178,7 +201,7 @@ inline int k_rotate_for(int K, int elem_bytes) { return MOE_K_ROTATE && ((int64_
 // then the BN/2 up rows of the same output columns, and each wave owns matching gate and up
 // accumulators.
 template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
-          bool BUF>
+          bool BUF, bool AQ>
 __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(MOE_GEMM_MIN_WAVES)))
 void mlp_gemm_kernel(GemmArgs args) {
   constexpr int NTH = WM * WN * 64;
@@ -209,9 +232,14 @@ void mlp_gemm_kernel(GemmArgs args) {
   const T* __restrict__ A = static_cast<const T*>(args.A);
   const T* __restrict__ W = static_cast<const T*>(args.W);
   T* __restrict__ Out = static_cast<T*>(args.Out);
+  // AQ: A holds E4M3 codes (one byte per element) with one power-of-two scale per 128 elements of a
+  // row; each vector of 8 codes is decoded to bf16 on its way into LDS
+  static_assert(!AQ || (BUF && sizeof(T) == 2), "fp8 A needs buffer loads and a bf16 GEMM");
   constexpr int A_OOB = 0x7ffffff0;
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, BUF ? args.a_bytes : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)args.a_scale, (short)0, AQ ? args.s_bytes : 0, 0x00020000);
   const int El = args.El;
   const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
   const int total = args.plan[0] * n_tiles;
@@ -268,7 +296,7 @@ void mlp_gemm_kernel(GemmArgs args) {
     // past the tile or past N use an offset past the buffer, which the hardware answers with zeros and
     // no memory request (a tile of an expert with few rows then moves only its real rows)
     const T* a_src[A_VEC];
-    int a_off[A_VEC];
+    int a_off[A_VEC], s_off[A_VEC];
     int a_lds[A_VEC];
     bool a_ok[A_VEC];
 #pragma unroll
@@ -280,7 +308,8 @@ void mlp_gemm_kernel(GemmArgs args) {
       const int p = p0 + (a_ok[i] ? r : 0);
       const int src_row = args.a_perm ? args.a_perm[p] : p;
       a_src[i] = A + (int64_t)src_row * args.lda;
-      a_off[i] = (BUF && a_ok[i]) ? src_row * args.lda * (int)sizeof(T) : A_OOB;  // < a_bytes when BUF
+      a_off[i] = (BUF && a_ok[i]) ? src_row * args.lda * (AQ ? 1 : (int)sizeof(T)) : A_OOB;  // < a_bytes when BUF
+      s_off[i] = (AQ && a_ok[i]) ? src_row * (args.lda / 128) * 4 : A_OOB;                  // < s_bytes when AQ
     }
     const T* b_src[B_VEC];
     int b_off[B_VEC];
@@ -328,7 +357,14 @@ void mlp_gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int i = 0; i < A_VEC; ++i) {
         const int col = min(k0 + a_lds[i] % LDR, args.K - VN);
-        if (BUF) {
+        if (AQ) {
+          // 8 codes and the scale of their 128-element block; decoded in store_stage
+          const int vo = a_off[i] == A_OOB ? A_OOB : a_off[i] + col;
+          const int so = s_off[i] == A_OOB ? A_OOB : s_off[i] + (col >> 7) * 4;
+          const u32x2 c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(a_rsrc, vo, 0, 0));
+          const uint32_t sc = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, so, 0, 0));
+          xa[i] = u32x4{c.x, c.y, sc, 0u};
+        } else if (BUF) {
           const int vo = a_off[i] == A_OOB ? A_OOB : a_off[i] + col * (int)sizeof(T);
           xa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, vo, 0, 0));
         } else {
@@ -352,7 +388,10 @@ void mlp_gemm_kernel(GemmArgs args) {
     auto store_stage = [&](int st, int buf, const u32x4 (&xa)[A_VEC], const u32x4 (&xb)[B_VEC]) {
       const int k0 = kslice(st);
 #pragma unroll
-      for (int i = 0; i < A_VEC; ++i) st16(&As[buf][a_lds[i]], (a_ok[i] && k0 + a_lds[i] % LDR < args.K) ? xa[i] : zero);
+      for (int i = 0; i < A_VEC; ++i) {
+        const u32x4 v = AQ ? e4m3x8_to_bf16(xa[i]) : xa[i];
+        st16(&As[buf][a_lds[i]], (a_ok[i] && k0 + a_lds[i] % LDR < args.K) ? v : zero);
+      }
 #pragma unroll
       for (int i = 0; i < B_VEC; ++i) st16(&Bs[buf][b_lds[i]], (b_ok[i] && k0 + b_lds[i] % LDR < args.K) ? xb[i] : zero);
     };
@@ -684,12 +723,15 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
   }
 }
 
-template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT>
+template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
+          bool AQ = false>
 void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
-  if (a.a_bytes > 0 && a.w_bytes > 0)
-    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, true><<<grid, WM * WN * 64, 0, stream>>>(a);
+  if (AQ)  // the fp8 entry point has checked that every buffer fits buffer offsets
+    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, true, AQ><<<grid, WM * WN * 64, 0, stream>>>(a);
+  else if (a.a_bytes > 0 && a.w_bytes > 0)
+    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, true, false><<<grid, WM * WN * 64, 0, stream>>>(a);
   else
-    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, false><<<grid, WM * WN * 64, 0, stream>>>(a);
+    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, false, false><<<grid, WM * WN * 64, 0, stream>>>(a);
 }
 
 // Persistent grid sizes in workgroups per CU and the compute-bound tile shapes; overridable at compile
@@ -848,17 +890,17 @@ void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H
       dn, (int)h_bytes);
 }
 
-template <int BM>
+template <int BM, bool AQ>
 void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int El, int num_cus,
                    hipStream_t stream) {
   // with many local experts of few rows each, streaming (non-temporal) weight loads in the gate/up
   // pass measured faster; with few experts the default cache policy did
   const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_DEC_GU_BN / 2), num_cus, MOE_DEC_WPC);
   if (El >= MOE_DEC_NT_MIN_EXPERTS)
-    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true>(
+    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true, AQ>(
         gu, g1, stream);
   else
-    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, false>(
+    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, false, AQ>(
         gu, g1, stream);
   const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
   launch_gemm<bf16_t, Op16, BM, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB, false>(
@@ -869,18 +911,20 @@ void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, i
 // variants: 0 bf16 many rows per expert, register-staged; 1 and 5 bf16 few rows per expert (weight
 // streaming) with 32- and 64-row tiles; 2 fp32; 3 and 4 bf16 many rows per expert, direct-to-LDS with
 // 128- and 256-row tiles
-MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16) {
+MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16, int fp8_a) {
   if (!xdt_bf16) return MlpTiles{32, 2};
   const int64_t per_expert = El > 0 ? rows_max / El : rows_max;
   if (per_expert < 128) return per_expert >= MOE_DEC_TALL_MIN_ROWS ? MlpTiles{64, 5} : MlpTiles{32, 1};
-  if (!dl_fits(rows_max, H, F)) return MlpTiles{MOE_PRE_BM, 0};
+  // fp8 rows are decoded on their way through registers, so they take the register-staged tiles
+  if (fp8_a || !dl_fits(rows_max, H, F)) return MlpTiles{MOE_PRE_BM, 0};
   if (per_expert >= MOE_DL_TALL_MIN_ROWS) return MlpTiles{256, 4};
   return MlpTiles{128, 3};
 }
 
 hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
                              const void* w_down, int F, void* out_buf, int* plan, int* perm, void* hbuf,
-                             const MlpTiles& tiles, int num_cus, hipStream_t stream) {
+                             const MlpTiles& tiles, int num_cus, hipStream_t stream, const float* a_scale) {
+  const bool aq = a_scale != nullptr;
   const int El = L.E / L.R;
   const int H = L.H;
   const int64_t rows_max = moe_rows_max(L.T, L.k, L.E, L.C);
@@ -904,7 +948,9 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   gu.out_perm = nullptr;
   gu.plan = plan;
   gu.El = El;
-  gu.a_bytes = buffer_bytes(rows_max * H * (xdt_bf16 ? 2 : 4));
+  gu.a_bytes = buffer_bytes(rows_max * H * (aq ? 1 : (xdt_bf16 ? 2 : 4)));
+  gu.a_scale = a_scale;
+  gu.s_bytes = aq ? buffer_bytes(rows_max * (H / 128) * 4) : 0;
   gu.w_bytes = buffer_bytes(gu.w_stride * (xdt_bf16 ? 2 : 4));
   gu.k_rotate = k_rotate_for(H, xdt_bf16 ? 2 : 4);
 
@@ -937,16 +983,21 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
       break;
     case 0: {  // bf16, many rows per expert, operands staged through registers
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_PRE_BN / 2), num_cus, MOE_PRE_WPC);
-      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB, false>(gu, g1, stream);
+      if (aq)
+        launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB, false, true>(gu, g1, stream);
+      else
+        launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB, false>(gu, g1, stream);
       const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_PRE_BN), num_cus, MOE_PRE_WPC);
       launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, false, MOE_PRE_RS, MOE_PRE_LDB, false>(dn, g2, stream);
       break;
     }
     case 1:  // bf16, few rows per expert: stream the weights through 32- or 64-row tiles
-      launch_decode<32>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
+      if (aq) launch_decode<32, true>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
+      else launch_decode<32, false>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
       break;
     case 5:
-      launch_decode<64>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
+      if (aq) launch_decode<64, true>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
+      else launch_decode<64, false>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
       break;
     default: {  // fp32
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus, 2);

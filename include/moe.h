@@ -8,6 +8,8 @@
  *   moe_expert_mlp -> per-expert SwiGLU MLP over the dispatched rows (grouped bf16 MFMA GEMM)
  *   moe_combine    -> router-weighted sum of each token's expert outputs, back in token order
  *
+ * plus an fp8 variant of the dispatch and of the expert MLP (moe_dispatch_fp8, moe_expert_mlp_fp8).
+ *
  * Sources (cited by page title and section):
  *   [EPM] "Efficient and portable mixture-of-experts communication" (Perplexity, 2025)
  *   [EFA] "Enabling trillion-parameter models on AWS EFA" (Perplexity, 2025)
@@ -188,6 +190,50 @@ int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* la
  */
 int moe_combine(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout,
                 const float* topk_w, void* y, hipStream_t stream);
+
+/*
+ * fp8 block-scaled dispatch.
+ * [EPM] "Dispatch": the send side packs the tokens together with their block scale factors.
+ * [EFA] "Оценка": dispatch runs with fp8 block scaling, combine in bf16. The pages fix neither the fp8
+ * format nor the block or the scale; the readings here:
+ *   - codes: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite 448,
+ *     no infinities);
+ *   - one scale per MOE_FP8_BLOCK consecutive hidden elements of a row, a power of two 2^E with E the
+ *     smallest integer such that max|x| / 2^E <= 448 (E = 0 for an all-zero block);
+ *   - code = x / 2^E rounded to the nearest E4M3 value, ties to the even mantissa, magnitudes above 448
+ *     clamped to 448, sign kept for values rounding to zero;
+ *   - the value a code stands for, code * 2^E, is exactly a bfloat16 value.
+ */
+#define MOE_FP8_BLOCK 128
+
+/*
+ * moe_dispatch_fp8 -- moe_dispatch whose send rows are fp8 block-scaled instead of copies of x.
+ * The layout (counts, capacity drops, offsets, row_token / row_slot / pair_row) is exactly the one
+ * moe_dispatch writes; send row i holds x[row_token[i]] quantised as above.
+ *   x          [T, H] bf16 activations (xdt must be MOE_BF16); H % MOE_FP8_BLOCK == 0
+ *   topk_ids   [T, k] int32 expert ids
+ *   layout     as for moe_dispatch
+ *   send_q     [rows_max, H] uint8 E4M3 codes (output)
+ *   send_scale [rows_max, H / MOE_FP8_BLOCK] fp32 block scales (output), each a power of two
+ *   workspace  device scratch of at least moe_dispatch_workspace_bytes(T, k, E) bytes
+ */
+int moe_dispatch_fp8(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const moe_layout_t* layout,
+                     uint8_t* send_q, float* send_scale, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * moe_expert_mlp_fp8 -- moe_expert_mlp on fp8 block-scaled rows: each activation enters the gate/up
+ * GEMM as the bf16 value code * scale (exact); everything else is moe_expert_mlp in bf16.
+ *   send_q, send_scale  rows written by moe_dispatch_fp8
+ *   layout              the layout moe_dispatch_fp8 filled
+ *   w_gate_up, w_down   bf16 expert weights, as for moe_expert_mlp
+ *   out_buf             [rows_max, H] bf16 output, row-aligned with send_q (feeds moe_combine)
+ *   workspace           device scratch of at least moe_expert_mlp_workspace_bytes(T, k, E, R, C, F, MOE_BF16)
+ * Requires H % MOE_FP8_BLOCK == 0, F % 8 == 0, and each buffer below 2 GiB (else MOE_ERR_UNSUPPORTED).
+ */
+int moe_expert_mlp_fp8(const uint8_t* send_q, const float* send_scale, const moe_layout_t* layout,
+                       const void* w_gate_up, const void* w_down, int F, void* out_buf, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -68,3 +68,26 @@ def rowwise_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     with np.errstate(divide="ignore", invalid="ignore"):
         out = np.where(den > 0, num / np.where(den > 0, den, 1.0), np.where(num > 0, np.inf, 0.0))
     return out
+
+
+def run_layer_fp8(inp: dict, k: int, R: int, stream=None) -> dict:
+    """route -> fp8 block-scaled dispatch -> expert MLP on the fp8 rows -> combine (bf16 activations)."""
+    x = inp["x"]
+    dev = x.device
+    T, H = x.shape
+    E = inp["w_router"].shape[0]
+    C = inp["C"]
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    moe.moe_route(x, inp["w_router"], inp["bias"], k, logits, ids, w, stream=stream)
+    L = moe.Layout(T, k, E, R, C, H, device=dev)
+    send_q = torch.empty(L.rows_max, H, dtype=torch.uint8, device=dev)
+    send_scale = torch.empty(L.rows_max, H // moe.MOE_FP8_BLOCK, dtype=torch.float32, device=dev)
+    moe.moe_dispatch_fp8(x, ids, L, send_q, send_scale, stream=stream)
+    out_buf = torch.empty(L.rows_max, H, dtype=x.dtype, device=dev)
+    moe.moe_expert_mlp_fp8(send_q, send_scale, L, inp["w_gate_up"], inp["w_down"], out_buf, stream=stream)
+    y = torch.empty(T, H, dtype=x.dtype, device=dev)
+    moe.moe_combine(out_buf, L, w, y, stream=stream)
+    torch.cuda.synchronize()
+    return dict(logits=logits, ids=ids, w=w, layout=L, send_q=send_q, send_scale=send_scale, out_buf=out_buf, y=y)

@@ -21,7 +21,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails before an
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -138,6 +138,27 @@ def test_mlp_and_combine_reject_invalid_arguments(lib):
     assert lib.moe_combine(FAKE, moe.MOE_BF16, ctypes.byref(L), None, FAKE, None) == MOE_ERR_INVALID
     assert lib.moe_combine(FAKE, 5, ctypes.byref(L), FAKE, FAKE, None) == MOE_ERR_UNSUPPORTED
     assert lib.moe_combine(FAKE, moe.MOE_BF16, ctypes.byref(_layout(E=0)), FAKE, FAKE, None) == MOE_ERR_INVALID
+
+
+def test_fp8_entry_points_reject_invalid_arguments(lib):
+    def disp(L, xdt=moe.MOE_BF16, q=FAKE, sc=FAKE, ws=FAKE, wsb=1 << 30):
+        return lib.moe_dispatch_fp8(FAKE, xdt, FAKE, ctypes.byref(L), q, sc, ws, wsb, None)
+    assert disp(_layout(H=128), xdt=moe.MOE_F32) == MOE_ERR_UNSUPPORTED   # fp8 rows come from bf16 x
+    assert disp(_layout(H=64)) == MOE_ERR_UNSUPPORTED                     # H not a multiple of the block
+    assert disp(_layout(H=128), q=None) == MOE_ERR_INVALID
+    assert disp(_layout(H=128), sc=None) == MOE_ERR_INVALID
+    assert disp(_layout(H=128), ws=None) == MOE_ERR_INVALID
+    assert disp(_layout(H=128, k=9, E=16)) == MOE_ERR_INVALID
+
+    def mlp(L, sc=FAKE, F=64, wgu=FAKE, ws=FAKE, wsb=1 << 30):
+        return lib.moe_expert_mlp_fp8(FAKE, sc, ctypes.byref(L), wgu, FAKE, F, FAKE, ws, wsb, None)
+    assert mlp(_layout(H=64)) == MOE_ERR_UNSUPPORTED
+    assert mlp(_layout(H=128), sc=None) == MOE_ERR_INVALID
+    assert mlp(_layout(H=128), F=12) == MOE_ERR_UNSUPPORTED
+    assert mlp(_layout(H=128), wgu=None) == MOE_ERR_INVALID
+    assert mlp(_layout(H=128), wsb=8) == MOE_ERR_INVALID
+    # weights beyond 31-bit buffer offsets are refused rather than read with a wrapped offset
+    assert mlp(_layout(H=65536), F=32768) == MOE_ERR_UNSUPPORTED
 
 
 def _py_sources(folder):
