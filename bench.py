@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default=None,
                     help="workload name or number (default: mixtral8x7b-decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--fp8-dispatch", action="store_true",
+                    help="dispatch fp8 block-scaled rows (E4M3 codes, one power-of-two scale per 128 hidden "
+                         "elements) and run the expert MLP on them; combine stays bf16 (bf16 workloads only)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (3 times), the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters, and exit")
@@ -147,22 +150,25 @@ def pick_workload(name):
     raise SystemExit(f"unknown workload {name!r}; choose from {[c.name for c in W.CONFIGS.values()]}")
 
 
-def algorithmic_bytes(cfg, C, counts, s):
-    """Bytes each stage must move (what the method needs, not what the kernels happen to move)."""
+def algorithmic_bytes(cfg, C, counts, s, fp8=False):
+    """Bytes each stage must move (what the method needs, not what the kernels happen to move).
+
+    fp8: the send rows are one byte per element plus a 4-byte scale per 128 elements."""
     T, H, E, k, F, El = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.El
+    q = (H + 4 * (H // 128)) if fp8 else H * s       # bytes of one send row
     kept = counts["kept"]
     touched = counts["tokens_touched"]
     active_local = counts["active_local"]
     bias = 0 if counts["bias_stride"] is None else (E * 4 if counts["bias_stride"] == 0 else T * E * 4)
     route = T * H * s + E * H * 4 + bias + T * E * 4 + T * k * 8
-    dispatch = touched * H * s + kept * H * s + kept * 8 + 2 * T * k * 4 + E * 16
+    dispatch = touched * H * s + kept * q + kept * 8 + 2 * T * k * 4 + E * 16
     combine = kept * H * s + T * k * 8 + T * H * s
-    mlp = active_local * 3 * H * F * s + 2 * kept * H * s
+    mlp = active_local * 3 * H * F * s + kept * q + kept * H * s
     return dict(route=route, dispatch=dispatch, combine=combine, mlp=mlp,
                 route_flops=2 * T * E * H, mlp_flops=6 * H * F * kept)
 
 
-def cpu_baseline(cfg, inp_dev, max_tokens=None):
+def cpu_baseline(cfg, inp_dev, max_tokens=None, fp8=False):
     """Time the CPU oracle (as it stands) on the first tokens of the same workload."""
     import numpy as np
     import torch
@@ -192,10 +198,14 @@ def cpu_baseline(cfg, inp_dev, max_tokens=None):
     wdn = host(inp_dev["w_down"])
     C = W.capacity(cfg, T)
     t0 = time.perf_counter()
-    res = oracle.moe_layer(x, dt, wr, bias, cfg.k, C, cfg.R, wgu, wdn, cfg.F)
+    if fp8:
+        res = oracle.fp8.moe_layer_fp8(x, wr, bias, cfg.k, C, cfg.R, wgu, wdn, cfg.F)
+    else:
+        res = oracle.moe_layer(x, dt, wr, bias, cfg.k, C, cfg.R, wgu, wdn, cfg.F)
     sec = time.perf_counter() - t0
-    sample = (f"the whole {cfg.name} batch ({T} tokens, one oracle run)" if T == cfg.T else
-              f"the first {T} of {cfg.T} tokens of {cfg.name} as one batch (capacity {C}), one oracle run")
+    what = " with fp8 dispatch" if fp8 else ""
+    sample = (f"the whole {cfg.name} batch ({T} tokens, one oracle run{what})" if T == cfg.T else
+              f"the first {T} of {cfg.T} tokens of {cfg.name} as one batch (capacity {C}), one oracle run{what}")
     return dict(value=T / sec, unit="tokens/s", cores=int(threads), kind="oracle", sample=sample,
                 seconds=round(sec, 3), rows=int(res["layout"].total))
 
@@ -231,6 +241,9 @@ def main():
     C = inp["C"]
     x = inp["x"]
     s = x.element_size()
+    fp8 = args.fp8_dispatch
+    if fp8 and (x.dtype != torch.bfloat16 or H % moe.MOE_FP8_BLOCK):
+        raise SystemExit(f"--fp8-dispatch needs bf16 activations and H % {moe.MOE_FP8_BLOCK} == 0")
 
     # every buffer and workspace is allocated once, outside the timed region
     logits = torch.empty(T, E, dtype=torch.float32, device=dev)
@@ -239,6 +252,9 @@ def main():
     L = moe.Layout(T, k, E, R, C, H, device=dev)
     send_buf = torch.empty(L.rows_max, H, dtype=x.dtype, device=dev)
     out_buf = torch.empty_like(send_buf)
+    if fp8:
+        send_q = torch.empty(L.rows_max, H, dtype=torch.uint8, device=dev)
+        send_scale = torch.empty(L.rows_max, H // moe.MOE_FP8_BLOCK, dtype=torch.float32, device=dev)
     y = torch.empty(T, H, dtype=x.dtype, device=dev)
     xdt = moe.MOE_BF16 if x.dtype == torch.bfloat16 else moe.MOE_F32
     ws_route = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E, xdt)), dtype=torch.uint8, device=dev)
@@ -254,12 +270,18 @@ def main():
         moe.moe_route(x, inp["w_router"], inp["bias"], k, logits, ids, wts, workspace=ws_route)
         if ev is not None:
             ev[1].record(stream)
-        moe.moe_dispatch(x, ids, L, send_buf, workspace=ws_disp)
+        if fp8:
+            moe.moe_dispatch_fp8(x, ids, L, send_q, send_scale, workspace=ws_disp)
+        else:
+            moe.moe_dispatch(x, ids, L, send_buf, workspace=ws_disp)
         if ev is not None:
             ev[2].record(stream)
         if mlp_ev is not None:
             mlp_ev[0].record(stream)
-        moe.moe_expert_mlp(send_buf, L, inp["w_gate_up"], inp["w_down"], out_buf, workspace=ws_mlp)
+        if fp8:
+            moe.moe_expert_mlp_fp8(send_q, send_scale, L, inp["w_gate_up"], inp["w_down"], out_buf, workspace=ws_mlp)
+        else:
+            moe.moe_expert_mlp(send_buf, L, inp["w_gate_up"], inp["w_down"], out_buf, workspace=ws_mlp)
         if ev is not None:
             ev[3].record(stream)
         if mlp_ev is not None:
@@ -306,7 +328,7 @@ def main():
     touched = int((pr >= 0).any(dim=1).sum().item())
     counts = dict(kept=kept, tokens_touched=touched, active_local=active_local,
                   bias_stride=None if inp["bias"] is None else inp["bias_stride"])
-    ab = algorithmic_bytes(cfg, C, counts, s)
+    ab = algorithmic_bytes(cfg, C, counts, s, fp8)
 
     mlp_s = mlp_us_timed * 1e-6
     mlp_ai = ab["mlp_flops"] / max(ab["mlp"], 1)
@@ -320,8 +342,9 @@ def main():
         achieved = ab["mlp"] / mlp_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
-    roof["traffic"] = measured_traffic(cfg.name)
-    roof["kernel"] = "moe_expert_mlp (grouped GEMM: plan + gate/up + down launches)"
+    roof["traffic"] = None if fp8 else measured_traffic(cfg.name)
+    roof["kernel"] = ("moe_expert_mlp_fp8" if fp8 else "moe_expert_mlp") + \
+        " (grouped GEMM: plan + gate/up + down launches)"
     roof["algorithmic_bytes"] = ab["mlp"]
     roof["algorithmic_flops"] = ab["mlp_flops"]
 
@@ -343,7 +366,8 @@ def main():
         "dtype": "bf16" if s == 2 else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "ffn": F,
-                   "dest_ranks": R, "capacity": C, "routing": cfg.routing, "act_dtype": cfg.dtype},
+                   "dest_ranks": R, "capacity": C, "routing": cfg.routing, "act_dtype": cfg.dtype,
+                   "dispatch_payload": "fp8-e4m3-block128" if fp8 else cfg.dtype},
         "roofline": roof,
         "expert_mlp_us_timed": round(mlp_us_timed, 2),
         "stages_us": {n: round(v, 2) for n, v in stage_us.items()},
@@ -360,7 +384,7 @@ def main():
     if not args.no_cpu_baseline:
         sample_tokens = None if cfg.T <= 512 else 256
         print(f"[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, sample_tokens, fp8)
     print(json.dumps(result), flush=True)
 
 

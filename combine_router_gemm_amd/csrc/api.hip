@@ -147,17 +147,11 @@ int expert_mlp(const void* send_buf, const float* a_scale, moe_dtype_t xdt, cons
   int* perm = reinterpret_cast<int*>(ws);
   ws += moe::align256((size_t)rows * sizeof(int));
   void* hbuf = ws;
-  const moe::MlpTiles tiles = moe::mlp_pick_tiles(rows, El, L.H, F, xdt == MOE_BF16, a_scale != nullptr);
+  const moe::MlpTiles tiles = moe::mlp_pick_tiles(rows, El, L.H, F, xdt == MOE_BF16);
   return hip_status(moe::launch_expert_mlp(send_buf, xdt == MOE_BF16, L, w_gate_up, w_down, F, out_buf, plan, perm,
                                            hbuf, tiles, device_cus(), stream, a_scale));
 }
 
-// fp8 rows and weights must fit 31-bit buffer offsets (the fp8 GEMM path reads them with buffer loads)
-bool fp8_fits(int64_t rows, int H, int F) {
-  const int64_t lim = 0x7ffffff0ll - 256;
-  return rows * (int64_t)H < lim && rows * (int64_t)(H / MOE_FP8_BLOCK) * 4 < lim && rows * (int64_t)F * 2 < lim &&
-         (int64_t)2 * F * H * 2 < lim && (int64_t)H * F * 2 < lim;
-}
 }  // namespace
 
 int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* layout, const void* w_gate_up,
@@ -196,7 +190,6 @@ int moe_expert_mlp_fp8(const uint8_t* send_q, const float* send_scale, const moe
   if (L.H % MOE_FP8_BLOCK != 0) return MOE_ERR_UNSUPPORTED;
   const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
   if (rows > 0 && !send_scale) return MOE_ERR_INVALID;
-  if (F >= 1 && F % 8 == 0 && !fp8_fits(rows, L.H, F)) return MOE_ERR_UNSUPPORTED;
   // with no rows there is nothing to decode: the bf16 path launches only the (empty) plan
   return expert_mlp(send_q, rows > 0 ? send_scale : nullptr, MOE_BF16, layout, w_gate_up, w_down, F, out_buf,
                     workspace, workspace_bytes, stream);

@@ -211,12 +211,15 @@ __global__ __launch_bounds__(DS_THREADS) void dispatch_scan_kernel(int* __restri
 // (lane + 64 i, one pass per 64 * VPL slices) and stores each to every kept row with non-temporal
 // stores. A token whose pairs were all dropped is not read.
 constexpr int SCATTER_WAVES = 4;
+constexpr int FP8_SPLIT_TOKENS = 1024;
 
-// Row of pair (t, lane) for lanes < k (-1 if dropped or not a pair), with the layout entries written.
+// Row of pair (t, lane) for lanes < k (-1 if dropped or not a pair), with the layout entries written
+// when `write` is set.
 __device__ __forceinline__ int resolve_pair_row(int t, int lane, const int* __restrict__ ids, int k, int E, int C,
                                                 const int* __restrict__ blk_base, const int* __restrict__ pair_local,
                                                 const int* __restrict__ offset, int* __restrict__ row_token,
-                                                int* __restrict__ row_slot, int* __restrict__ pair_row) {
+                                                int* __restrict__ row_slot, int* __restrict__ pair_row,
+                                                bool write = true) {
   int row = -1;
   if (lane < k) {
     const int64_t p = (int64_t)t * k + lane;
@@ -226,10 +229,12 @@ __device__ __forceinline__ int resolve_pair_row(int t, int lane, const int* __re
       const int pos = blk_base[(int64_t)(t / DISPATCH_TB) * E + e] + local;
       if (pos < C) row = offset[e] + pos;
     }
-    pair_row[p] = row;
-    if (row >= 0) {
-      row_token[row] = t;
-      row_slot[row] = lane;
+    if (write) {
+      pair_row[p] = row;
+      if (row >= 0) {
+        row_token[row] = t;
+        row_slot[row] = lane;
+      }
     }
   }
   return row;
@@ -278,23 +283,12 @@ void launch_scatter_t(const void* x, const int* ids, const moe_layout_t& L, void
 }
 
 // ---- fp8 block-scaled rows ----
-// OCP E4M3 code of y (|y| <= 448 after clamping), nearest value with ties to the even mantissa, sign
-// kept. Below 2^-6 the quantum is 2^-9, so the code is y * 2^9 rounded (8 there is the smallest normal,
-// whose code is 8 too); above, the fp32 fraction is rounded to 3 bits, carrying into the exponent.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = __float_as_uint(y) >> 31;
-  const float a = fminf(fabsf(y), 448.0f);
-  uint32_t code;
-  if (a < 0.015625f) {
-    code = (uint32_t)rintf(a * 512.0f);
-  } else {
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);
-    b &= ~0xFFFFFu;
-    const int e = (int)(b >> 23) - 127;  // -6 .. 8
-    code = ((uint32_t)(e + 7) << 3) | ((b >> 20) & 7u);
-  }
-  return code | (sign << 7);
+// OCP E4M3 codes of four values |y| <= 448, packed little-endian: v_cvt_pk_fp8_f32 rounds to the nearest
+// E4M3 value, ties to the even mantissa, and keeps the sign of a value that rounds to zero (gfx950
+// writes OCP E4M3).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // Exponent E of the block scale: the smallest integer with amax / 2^E <= 448. With amax = f * 2^fe,
@@ -306,10 +300,12 @@ __device__ __forceinline__ int e4m3_block_exp(float amax) {
   return fe - 9 + (f > 0.875f ? 1 : 0);
 }
 
-// One wave per token (as dispatch_scatter). A pass covers 64 * VPL 16-byte chunks of 8 bf16 values; a
-// 128-element block is 16 chunks held by 16 consecutive lanes, which find the block maximum with
-// shuffles. Each lane stores its 8 codes (8 bytes) to every kept row; the block's first lane stores
-// the scale.
+// One wave per (token, row segment): blockIdx.y picks the segment, gridDim.y segments split the row
+// (one segment when there are tokens enough to fill the GPU; with few tokens the encoding work of a row
+// is spread over more waves), and only segment 0 writes the layout entries. A pass covers 64 * VPL
+// 16-byte chunks of 8 bf16 values; a 128-element block is 16 chunks held by 16 consecutive lanes, which
+// find the block maximum with shuffles. Each lane stores its 8 codes (8 bytes) to every kept row; the
+// block's first lane stores the scale.
 template <int VPL>
 __global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_fp8_kernel(
     const bf16_t* __restrict__ x, const int* __restrict__ ids, int T_, int H, int k, int E, int C,
@@ -319,13 +315,14 @@ __global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_fp8_kerne
   const int lane = lane_id();
   const int t = blockIdx.x * SCATTER_WAVES + (int)(threadIdx.x >> 6);
   if (t >= T_) return;
-  const int row = resolve_pair_row(t, lane, ids, k, E, C, blk_base, pair_local, offset, row_token, row_slot, pair_row);
+  const int row = resolve_pair_row(t, lane, ids, k, E, C, blk_base, pair_local, offset, row_token, row_slot, pair_row,
+                                   blockIdx.y == 0);
   const uint64_t kept = __ballot(row >= 0);
   if (kept == 0) return;
   const int nvec = H / 8;  // H % 128 == 0, so every pass holds whole blocks
   const int nblk = H / 128;
   const bf16_t* src = x + (int64_t)t * H;
-  for (int base = 0; base < nvec; base += 64 * VPL) {
+  for (int base = blockIdx.y * 64 * VPL; base < nvec; base += gridDim.y * 64 * VPL) {
     u32x4 val[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -347,11 +344,11 @@ __global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_fp8_kerne
       for (int off = 8; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off, 64));
       const int E8 = e4m3_block_exp(am);
       sc[i] = ldexpf(1.0f, E8);
-      uint32_t c[8];
+      float y[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = e4m3_code(ldexpf(f[j], -E8));  // exact scaling by 2^-E
-      q[i].x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-      q[i].y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      for (int j = 0; j < 8; ++j) y[j] = ldexpf(f[j], -E8);  // exact scaling by 2^-E, |y| <= 448
+      q[i].x = e4m3x4(y[0], y[1], y[2], y[3]);
+      q[i].y = e4m3x4(y[4], y[5], y[6], y[7]);
     }
     for (uint64_t m = kept; m; m &= m - 1) {
       const int j = __builtin_ctzll(m);
@@ -418,13 +415,16 @@ hipError_t launch_dispatch_fp8(const void* x, const int* ids, const moe_layout_t
   if (st != hipSuccess || L.T == 0) return st;
   const int nvec = L.H / 8;
   const unsigned blocks = (unsigned)ceil_div_host(L.T, SCATTER_WAVES);
+  // with fewer tokens than FP8_SPLIT_TOKENS, segments of 64 chunks (one per lane) split each row
+  const bool split = L.T < FP8_SPLIT_TOKENS;
+  const dim3 grid(blocks, split ? (unsigned)std::min(ceil_div_host(nvec, 64), 65535) : 1u);  // y stride covers the rest
 #define MOE_SCATTER_FP8(VPL)                                                                                 \
-  dispatch_scatter_fp8_kernel<VPL><<<blocks, SCATTER_WAVES * 64, 0, stream>>>(                              \
+  dispatch_scatter_fp8_kernel<VPL><<<grid, SCATTER_WAVES * 64, 0, stream>>>(                                \
       static_cast<const bf16_t*>(x), ids, L.T, L.H, L.k, L.E, L.C, blk_count, pair_local, L.expert_offset,       \
       L.row_token, L.row_slot, L.pair_row, send_q, send_scale)
-  if (nvec > 256) MOE_SCATTER_FP8(16);
-  else if (nvec > 64) MOE_SCATTER_FP8(4);
-  else MOE_SCATTER_FP8(1);
+  if (split || nvec <= 64) MOE_SCATTER_FP8(1);
+  else if (nvec > 256) MOE_SCATTER_FP8(16);
+  else MOE_SCATTER_FP8(4);
 #undef MOE_SCATTER_FP8
   return hipGetLastError();
 }

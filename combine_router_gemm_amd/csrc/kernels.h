@@ -37,9 +37,10 @@ struct MlpTiles {
   int BM;       // rows per tile (shared by both GEMMs; the plan is built for it)
   int variant;  // kernel family, see mlp.hip
 };
-MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16, int fp8_a);
+MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16);
 size_t mlp_plan_ints(int El);
-// a_scale != nullptr: send_buf holds E4M3 codes with these block scales (bf16 GEMM on the decoded rows)
+// a_scale != nullptr: send_buf holds E4M3 codes with these block scales; they are expanded to bf16 in
+// out_buf first and the bf16 GEMMs read them from there
 hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
                              const void* w_down, int F, void* out_buf, int* plan, int* perm, void* hbuf,
                              const MlpTiles& tiles, int num_cus, hipStream_t stream, const float* a_scale);

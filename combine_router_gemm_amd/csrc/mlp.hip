@@ -162,29 +162,56 @@ struct GemmArgs {
   int a_bytes;          // bytes of A (rows_max x lda elements) when it fits 31-bit buffer offsets, else 0
   int w_bytes;          // bytes of one expert's weights (w_stride elements), same rule
   int k_rotate;         // start each tile's K loop at a tile-dependent stage (see k_rotation)
-  const float* a_scale; // fp8 A only: [rows, lda / 128] power-of-two block scales
-  int s_bytes;          // bytes of a_scale
 };
 
-// Value of an OCP E4M3 code (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 is
-// subnormal, 2^-6 * m/8). The codes the fp8 dispatch writes are never NaN.
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-  return (c & 0x80u) ? -mag : mag;
-}
-
-// Eight E4M3 codes (q.x, q.y, little-endian bytes) times their block scale (q.z, a power of two) as
-// eight bf16 values: code * scale has at most 4 significant bits, so the bf16 rounding is exact.
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x4 q) {
-  const float sc = __uint_as_float(q.z);
+// Eight OCP E4M3 codes (q.x, q.y, little-endian bytes) times their block scale sc (a power of two) as
+// eight bf16 values. v_cvt_pk_f32_fp8 decodes two codes exactly (gfx950 reads them as OCP E4M3); code *
+// scale has at most 4 significant bits, so the product and its bf16 rounding are exact.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t qx, uint32_t qy, float sc) {
   float f[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f[j] = e4m3_value((q.x >> (8 * j)) & 0xFFu) * sc;
-    f[4 + j] = e4m3_value((q.y >> (8 * j)) & 0xFFu) * sc;
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w = h ? qy : qx;
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[4 * h + 0] = lo.x * sc;
+    f[4 * h + 1] = lo.y * sc;
+    f[4 * h + 2] = hi.x * sc;
+    f[4 * h + 3] = hi.y * sc;
   }
   return pack(f);
+}
+
+// fp8 rows (E4M3 codes with one power-of-two scale per 128 elements) expanded to bf16 rows, for GEMM
+// tiles that load their A operand straight into LDS. A chunk is 16 codes at flat index 16 c of the first
+// *total_rows rows; with H % 128 == 0 the flat index / 128 is also the flat index of the block's scale
+// in [rows, H / 128]. Each thread expands FP8_EXPAND_CHUNKS chunks, all loads issued before any store.
+constexpr int FP8_EXPAND_CHUNKS = 4;
+__global__ __launch_bounds__(256) void fp8_rows_to_bf16_kernel(const uint8_t* __restrict__ q,
+                                                               const float* __restrict__ scale,
+                                                               const int* __restrict__ total_rows, int H,
+                                                               bf16_t* __restrict__ out) {
+  const int64_t n = (int64_t)(*total_rows) * (H / 16);
+  const int64_t c0 = (int64_t)blockIdx.x * (256 * FP8_EXPAND_CHUNKS) + threadIdx.x;
+  if (c0 >= n) return;
+  u32x4 c[FP8_EXPAND_CHUNKS];
+  float sc[FP8_EXPAND_CHUNKS];
+#pragma unroll
+  for (int u = 0; u < FP8_EXPAND_CHUNKS; ++u) {
+    const int64_t ci = c0 + u * 256;
+    if (ci < n) {
+      c[u] = ld16_nt(q + ci * 16);
+      sc[u] = scale[ci >> 3];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < FP8_EXPAND_CHUNKS; ++u) {
+    const int64_t ci = c0 + u * 256;
+    if (ci < n) {
+      st16(out + ci * 16, e4m3x8_to_bf16(c[u].x, c[u].y, sc[u]));
+      st16(out + ci * 16 + 8, e4m3x8_to_bf16(c[u].z, c[u].w, sc[u]));
+    }
+  }
 }
 
 // Weight rows whose pitch is a multiple of 8 KB put the same K slice of every row of a tile on the same
@@ -201,7 +228,7 @@ inline int k_rotate_for(int K, int elem_bytes) { return MOE_K_ROTATE && ((int64_
 // then the BN/2 up rows of the same output columns, and each wave owns matching gate and up
 // accumulators.
 template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
-          bool BUF, bool AQ>
+          bool BUF>
 __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(MOE_GEMM_MIN_WAVES)))
 void mlp_gemm_kernel(GemmArgs args) {
   constexpr int NTH = WM * WN * 64;
@@ -232,14 +259,9 @@ void mlp_gemm_kernel(GemmArgs args) {
   const T* __restrict__ A = static_cast<const T*>(args.A);
   const T* __restrict__ W = static_cast<const T*>(args.W);
   T* __restrict__ Out = static_cast<T*>(args.Out);
-  // AQ: A holds E4M3 codes (one byte per element) with one power-of-two scale per 128 elements of a
-  // row; each vector of 8 codes is decoded to bf16 on its way into LDS
-  static_assert(!AQ || (BUF && sizeof(T) == 2), "fp8 A needs buffer loads and a bf16 GEMM");
   constexpr int A_OOB = 0x7ffffff0;
   const __amdgpu_buffer_rsrc_t a_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, BUF ? args.a_bytes : 0, 0x00020000);
-  const __amdgpu_buffer_rsrc_t s_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)args.a_scale, (short)0, AQ ? args.s_bytes : 0, 0x00020000);
   const int El = args.El;
   const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
   const int total = args.plan[0] * n_tiles;
@@ -296,7 +318,7 @@ void mlp_gemm_kernel(GemmArgs args) {
     // past the tile or past N use an offset past the buffer, which the hardware answers with zeros and
     // no memory request (a tile of an expert with few rows then moves only its real rows)
     const T* a_src[A_VEC];
-    int a_off[A_VEC], s_off[A_VEC];
+    int a_off[A_VEC];
     int a_lds[A_VEC];
     bool a_ok[A_VEC];
 #pragma unroll
@@ -308,8 +330,7 @@ void mlp_gemm_kernel(GemmArgs args) {
       const int p = p0 + (a_ok[i] ? r : 0);
       const int src_row = args.a_perm ? args.a_perm[p] : p;
       a_src[i] = A + (int64_t)src_row * args.lda;
-      a_off[i] = (BUF && a_ok[i]) ? src_row * args.lda * (AQ ? 1 : (int)sizeof(T)) : A_OOB;  // < a_bytes when BUF
-      s_off[i] = (AQ && a_ok[i]) ? src_row * (args.lda / 128) * 4 : A_OOB;                  // < s_bytes when AQ
+      a_off[i] = (BUF && a_ok[i]) ? src_row * args.lda * (int)sizeof(T) : A_OOB;  // < a_bytes when BUF
     }
     const T* b_src[B_VEC];
     int b_off[B_VEC];
@@ -357,14 +378,7 @@ void mlp_gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int i = 0; i < A_VEC; ++i) {
         const int col = min(k0 + a_lds[i] % LDR, args.K - VN);
-        if (AQ) {
-          // 8 codes and the scale of their 128-element block; decoded in store_stage
-          const int vo = a_off[i] == A_OOB ? A_OOB : a_off[i] + col;
-          const int so = s_off[i] == A_OOB ? A_OOB : s_off[i] + (col >> 7) * 4;
-          const u32x2 c = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(a_rsrc, vo, 0, 0));
-          const uint32_t sc = __builtin_bit_cast(uint32_t, __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, so, 0, 0));
-          xa[i] = u32x4{c.x, c.y, sc, 0u};
-        } else if (BUF) {
+        if (BUF) {
           const int vo = a_off[i] == A_OOB ? A_OOB : a_off[i] + col * (int)sizeof(T);
           xa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, vo, 0, 0));
         } else {
@@ -389,8 +403,7 @@ void mlp_gemm_kernel(GemmArgs args) {
       const int k0 = kslice(st);
 #pragma unroll
       for (int i = 0; i < A_VEC; ++i) {
-        const u32x4 v = AQ ? e4m3x8_to_bf16(xa[i]) : xa[i];
-        st16(&As[buf][a_lds[i]], (a_ok[i] && k0 + a_lds[i] % LDR < args.K) ? v : zero);
+        st16(&As[buf][a_lds[i]], (a_ok[i] && k0 + a_lds[i] % LDR < args.K) ? xa[i] : zero);
       }
 #pragma unroll
       for (int i = 0; i < B_VEC; ++i) st16(&Bs[buf][b_lds[i]], (b_ok[i] && k0 + b_lds[i] % LDR < args.K) ? xb[i] : zero);
@@ -723,15 +736,12 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
   }
 }
 
-template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
-          bool AQ = false>
+template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT>
 void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
-  if (AQ)  // the fp8 entry point has checked that every buffer fits buffer offsets
-    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, true, AQ><<<grid, WM * WN * 64, 0, stream>>>(a);
-  else if (a.a_bytes > 0 && a.w_bytes > 0)
-    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, true, false><<<grid, WM * WN * 64, 0, stream>>>(a);
+  if (a.a_bytes > 0 && a.w_bytes > 0)
+    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, true><<<grid, WM * WN * 64, 0, stream>>>(a);
   else
-    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, false, false><<<grid, WM * WN * 64, 0, stream>>>(a);
+    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, false><<<grid, WM * WN * 64, 0, stream>>>(a);
 }
 
 // Persistent grid sizes in workgroups per CU and the compute-bound tile shapes; overridable at compile
@@ -890,17 +900,17 @@ void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H
       dn, (int)h_bytes);
 }
 
-template <int BM, bool AQ>
+template <int BM>
 void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int El, int num_cus,
                    hipStream_t stream) {
   // with many local experts of few rows each, streaming (non-temporal) weight loads in the gate/up
   // pass measured faster; with few experts the default cache policy did
   const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_DEC_GU_BN / 2), num_cus, MOE_DEC_WPC);
   if (El >= MOE_DEC_NT_MIN_EXPERTS)
-    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true, AQ>(
+    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true>(
         gu, g1, stream);
   else
-    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, false, AQ>(
+    launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, false>(
         gu, g1, stream);
   const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
   launch_gemm<bf16_t, Op16, BM, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB, false>(
@@ -911,12 +921,11 @@ void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, i
 // variants: 0 bf16 many rows per expert, register-staged; 1 and 5 bf16 few rows per expert (weight
 // streaming) with 32- and 64-row tiles; 2 fp32; 3 and 4 bf16 many rows per expert, direct-to-LDS with
 // 128- and 256-row tiles
-MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16, int fp8_a) {
+MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16) {
   if (!xdt_bf16) return MlpTiles{32, 2};
   const int64_t per_expert = El > 0 ? rows_max / El : rows_max;
   if (per_expert < 128) return per_expert >= MOE_DEC_TALL_MIN_ROWS ? MlpTiles{64, 5} : MlpTiles{32, 1};
-  // fp8 rows are decoded on their way through registers, so they take the register-staged tiles
-  if (fp8_a || !dl_fits(rows_max, H, F)) return MlpTiles{MOE_PRE_BM, 0};
+  if (!dl_fits(rows_max, H, F)) return MlpTiles{MOE_PRE_BM, 0};
   if (per_expert >= MOE_DL_TALL_MIN_ROWS) return MlpTiles{256, 4};
   return MlpTiles{128, 3};
 }
@@ -924,7 +933,17 @@ MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16, in
 hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
                              const void* w_down, int F, void* out_buf, int* plan, int* perm, void* hbuf,
                              const MlpTiles& tiles, int num_cus, hipStream_t stream, const float* a_scale) {
-  const bool aq = a_scale != nullptr;
+  if (a_scale != nullptr && moe_rows_max(L.T, L.k, L.E, L.C) > 0) {
+    // fp8 rows: expand them to bf16 in out_buf (rows_max x H bf16, unused until the down GEMM writes it in
+    // a later launch) and run the bf16 GEMMs on them. Decoding inside the gate/up GEMM instead (codes
+    // through registers) measured slower on every workload: it rules out the direct-to-LDS tiles.
+    // one thread per FP8_EXPAND_CHUNKS chunks of the rows_max rows; those past the kept rows exit at once
+    const int64_t chunks = moe_rows_max(L.T, L.k, L.E, L.C) * (int64_t)(L.H / 16);
+    const int g = (int)ceil_div_host64(chunks, 256 * FP8_EXPAND_CHUNKS);
+    fp8_rows_to_bf16_kernel<<<g, 256, 0, stream>>>(static_cast<const uint8_t*>(send_buf), a_scale,
+                                                   L.expert_offset + L.E, L.H, static_cast<bf16_t*>(out_buf));
+    send_buf = out_buf;
+  }
   const int El = L.E / L.R;
   const int H = L.H;
   const int64_t rows_max = moe_rows_max(L.T, L.k, L.E, L.C);
@@ -948,9 +967,7 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   gu.out_perm = nullptr;
   gu.plan = plan;
   gu.El = El;
-  gu.a_bytes = buffer_bytes(rows_max * H * (aq ? 1 : (xdt_bf16 ? 2 : 4)));
-  gu.a_scale = a_scale;
-  gu.s_bytes = aq ? buffer_bytes(rows_max * (H / 128) * 4) : 0;
+  gu.a_bytes = buffer_bytes(rows_max * H * (xdt_bf16 ? 2 : 4));
   gu.w_bytes = buffer_bytes(gu.w_stride * (xdt_bf16 ? 2 : 4));
   gu.k_rotate = k_rotate_for(H, xdt_bf16 ? 2 : 4);
 
@@ -983,21 +1000,16 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
       break;
     case 0: {  // bf16, many rows per expert, operands staged through registers
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_PRE_BN / 2), num_cus, MOE_PRE_WPC);
-      if (aq)
-        launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB, false, true>(gu, g1, stream);
-      else
-        launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB, false>(gu, g1, stream);
+      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB, false>(gu, g1, stream);
       const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_PRE_BN), num_cus, MOE_PRE_WPC);
       launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, false, MOE_PRE_RS, MOE_PRE_LDB, false>(dn, g2, stream);
       break;
     }
     case 1:  // bf16, few rows per expert: stream the weights through 32- or 64-row tiles
-      if (aq) launch_decode<32, true>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
-      else launch_decode<32, false>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
+      launch_decode<32>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
       break;
     case 5:
-      if (aq) launch_decode<64, true>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
-      else launch_decode<64, false>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
+      launch_decode<64>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
       break;
     default: {  // fp32
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus, 2);

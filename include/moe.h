@@ -210,7 +210,8 @@ int moe_combine(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout
  * moe_dispatch_fp8 -- moe_dispatch whose send rows are fp8 block-scaled instead of copies of x.
  * The layout (counts, capacity drops, offsets, row_token / row_slot / pair_row) is exactly the one
  * moe_dispatch writes; send row i holds x[row_token[i]] quantised as above.
- *   x          [T, H] bf16 activations (xdt must be MOE_BF16); H % MOE_FP8_BLOCK == 0
+ *   x          [T, H] bf16 activations (xdt must be MOE_BF16), finite (the codes of a block holding an
+ *              infinity or NaN are unspecified); H % MOE_FP8_BLOCK == 0
  *   topk_ids   [T, k] int32 expert ids
  *   layout     as for moe_dispatch
  *   send_q     [rows_max, H] uint8 E4M3 codes (output)
@@ -223,13 +224,14 @@ int moe_dispatch_fp8(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, co
 
 /*
  * moe_expert_mlp_fp8 -- moe_expert_mlp on fp8 block-scaled rows: each activation enters the gate/up
- * GEMM as the bf16 value code * scale (exact); everything else is moe_expert_mlp in bf16.
+ * GEMM as the bf16 value code * scale (exact); everything else is moe_expert_mlp in bf16. The rows are
+ * first expanded to bf16 in out_buf, which the down GEMM then overwrites with the results.
  *   send_q, send_scale  rows written by moe_dispatch_fp8
  *   layout              the layout moe_dispatch_fp8 filled
  *   w_gate_up, w_down   bf16 expert weights, as for moe_expert_mlp
  *   out_buf             [rows_max, H] bf16 output, row-aligned with send_q (feeds moe_combine)
  *   workspace           device scratch of at least moe_expert_mlp_workspace_bytes(T, k, E, R, C, F, MOE_BF16)
- * Requires H % MOE_FP8_BLOCK == 0, F % 8 == 0, and each buffer below 2 GiB (else MOE_ERR_UNSUPPORTED).
+ * Requires H % MOE_FP8_BLOCK == 0 and F % 8 == 0 (else MOE_ERR_UNSUPPORTED).
  */
 int moe_expert_mlp_fp8(const uint8_t* send_q, const float* send_scale, const moe_layout_t* layout,
                        const void* w_gate_up, const void* w_down, int F, void* out_buf, void* workspace,

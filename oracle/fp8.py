@@ -112,3 +112,22 @@ def dispatch_fp8(x_bits, ids, E: int, C: int, R: int = 1):
     codes, scales = quantize_rows(send.reshape(len(send), -1)) if len(send) else (
         np.zeros((0, np.asarray(x_bits).shape[1]), np.uint8), np.zeros((0, np.asarray(x_bits).shape[1] // BLOCK), np.float32))
     return layout, codes, scales
+
+
+def moe_layer_fp8(x_bits, w_router, bias, k: int, C: int, R: int, w_gate_up, w_down, F: int, ids=None) -> dict:
+    """The layer with fp8 block-scaled dispatch and bf16 combine ("Enabling trillion-parameter models on
+    AWS EFA", section "Оценка"): route as moe.moe_layer, dispatch the rows as codes and scales, run the
+    expert MLP on the values the codes stand for, combine in bf16. bf16 activations only."""
+    from .moe import combine, expert_mlp, router_logits, routing_weights, row_experts, topk_select
+    logits = router_logits(x_bits, "bf16", w_router, bias)
+    if ids is None:
+        ids = topk_select(logits, k)
+    ids = np.asarray(ids, dtype=np.int32)
+    w = routing_weights(logits, ids)
+    E = np.asarray(w_router).shape[0]
+    layout, codes, scales = dispatch_fp8(x_bits, ids, E, C, R)
+    rows = dequantize_rows_bf16(codes, scales)
+    out_buf = expert_mlp(rows, "bf16", row_experts(layout.expert_offset, E), E // R, w_gate_up, w_down, F)
+    y = combine(out_buf, "bf16", layout.pair_row, w)
+    return dict(logits=logits, ids=ids, weights=w, layout=layout, send_q=codes, send_scale=scales,
+                out_buf=out_buf, y=y)

@@ -121,3 +121,33 @@ def test_dispatch_fp8_is_dispatch_then_quantize():
     for i, t in enumerate(lay.row_token):
         c1, s1 = fp8.quantize_rows(x[t:t + 1])
         assert np.array_equal(codes[i], c1[0]) and np.array_equal(scales[i], s1[0])
+
+
+def test_layer_fp8_equals_bf16_layer_when_rows_are_exact_fp8():
+    # rows built from E4M3 values times a power of two per block, each block holding 448 * 2^j: the
+    # quantisation is then lossless, so the fp8 layer must give the bf16 layer's output bit for bit
+    from oracle.moe import moe_layer
+    from oracle.numerics import f64_to_bf16_bits
+    rng = np.random.default_rng(7)
+    T, H, E, k, F, R, C = 40, 256, 8, 2, 32, 2, 9
+    codes = rng.integers(0, 0x7E, size=(T, H))
+    codes |= rng.integers(0, 2, size=(T, H)) << 7
+    codes[:, ::128] = 0x7E
+    j = rng.integers(-12, -4, size=(T, H // 128))
+    v = fp8.e4m3_decode(codes).reshape(T, H // 128, 128) * np.ldexp(1.0, j)[:, :, None]
+    x = f64_to_bf16_bits(v.reshape(T, H))
+    assert np.array_equal(fp8.dequantize_rows(*fp8.quantize_rows(x)), bf16_bits_to_f64(x))
+    wr = rng.standard_normal((E, H)).astype(np.float32) * 0.02
+    wgu = f64_to_bf16_bits(rng.standard_normal((E // R, 2 * F, H)) * 0.05)
+    wdn = f64_to_bf16_bits(rng.standard_normal((E // R, H, F)) * 0.05)
+    ref = moe_layer(x, "bf16", wr, None, k, C, R, wgu, wdn, F)
+    got = fp8.moe_layer_fp8(x, wr, None, k, C, R, wgu, wdn, F)
+    assert ref["layout"].total < T * k                      # some pairs dropped by capacity
+    assert np.array_equal(got["y"], ref["y"]) and np.array_equal(got["out_buf"], ref["out_buf"])
+    # and with inexact rows the two differ, by no more than the fp8 rounding allows
+    x2 = _bf16_rows((T, H), 8)
+    a = bf16_bits_to_f64(moe_layer(x2, "bf16", wr, None, k, C, R, wgu, wdn, F)["y"])
+    b = bf16_bits_to_f64(fp8.moe_layer_fp8(x2, wr, None, k, C, R, wgu, wdn, F)["y"])
+    live = np.linalg.norm(a, axis=1) > 0
+    rel = np.linalg.norm(a - b, axis=1)[live] / np.linalg.norm(a, axis=1)[live]
+    assert 0 < rel.max() <= 0.1
