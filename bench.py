@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default=None,
                     help="workload name or number (default: mixtral8x7b-decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--sender-accumulate", action="store_true",
+                    help="combine with sender-side partial accumulation (moe_combine_send + moe_combine_recv): "
+                         "one partial row per (destination rank, token) instead of one row per kept pair")
     ap.add_argument("--fp8-dispatch", action="store_true",
                     help="dispatch fp8 block-scaled rows (E4M3 codes, one power-of-two scale per 128 hidden "
                          "elements) and run the expert MLP on them; combine stays bf16 (bf16 workloads only)")
@@ -150,10 +153,12 @@ def pick_workload(name):
     raise SystemExit(f"unknown workload {name!r}; choose from {[c.name for c in W.CONFIGS.values()]}")
 
 
-def algorithmic_bytes(cfg, C, counts, s, fp8=False):
+def algorithmic_bytes(cfg, C, counts, s, fp8=False, sender=False):
     """Bytes each stage must move (what the method needs, not what the kernels happen to move).
 
-    fp8: the send rows are one byte per element plus a 4-byte scale per 128 elements."""
+    fp8: the send rows are one byte per element plus a 4-byte scale per 128 elements.
+    sender: combine writes one partial row per (rank, token) and reads it back, on top of the kept rows
+    and the output."""
     T, H, E, k, F, El = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.El
     q = (H + 4 * (H // 128)) if fp8 else H * s       # bytes of one send row
     kept = counts["kept"]
@@ -163,6 +168,8 @@ def algorithmic_bytes(cfg, C, counts, s, fp8=False):
     route = T * H * s + E * H * 4 + bias + T * E * 4 + T * k * 8
     dispatch = touched * H * s + kept * q + kept * 8 + 2 * T * k * 4 + E * 16
     combine = kept * H * s + T * k * 8 + T * H * s
+    if sender:
+        combine += 2 * counts["partial_rows"] * H * s + T * k * 4
     mlp = active_local * 3 * H * F * s + kept * q + kept * H * s
     return dict(route=route, dispatch=dispatch, combine=combine, mlp=mlp,
                 route_flops=2 * T * E * H, mlp_flops=6 * H * F * kept)
@@ -242,6 +249,7 @@ def main():
     x = inp["x"]
     s = x.element_size()
     fp8 = args.fp8_dispatch
+    sender = args.sender_accumulate
     if fp8 and (x.dtype != torch.bfloat16 or H % moe.MOE_FP8_BLOCK):
         raise SystemExit(f"--fp8-dispatch needs bf16 activations and H % {moe.MOE_FP8_BLOCK} == 0")
 
@@ -256,6 +264,7 @@ def main():
         send_q = torch.empty(L.rows_max, H, dtype=torch.uint8, device=dev)
         send_scale = torch.empty(L.rows_max, H // moe.MOE_FP8_BLOCK, dtype=torch.float32, device=dev)
     y = torch.empty(T, H, dtype=x.dtype, device=dev)
+    partial = torch.empty(R, T, H, dtype=x.dtype, device=dev) if sender else None
     xdt = moe.MOE_BF16 if x.dtype == torch.bfloat16 else moe.MOE_F32
     ws_route = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E, xdt)), dtype=torch.uint8, device=dev)
     ws_disp = torch.empty(max(1, moe.moe_dispatch_workspace_bytes(T, k, E)), dtype=torch.uint8, device=dev)
@@ -286,7 +295,11 @@ def main():
             ev[3].record(stream)
         if mlp_ev is not None:
             mlp_ev[1].record(stream)
-        moe.moe_combine(out_buf, L, wts, y)
+        if sender:
+            moe.moe_combine_send(out_buf, L, wts, partial)
+            moe.moe_combine_recv(partial, L, y)
+        else:
+            moe.moe_combine(out_buf, L, wts, y)
         if ev is not None:
             ev[4].record(stream)
 
@@ -326,9 +339,14 @@ def main():
     active_local = int((kept_per_e.view(R, cfg.El).sum(0) > 0).sum().item())
     pr = L.pair_row.cpu()
     touched = int((pr >= 0).any(dim=1).sum().item())
-    counts = dict(kept=kept, tokens_touched=touched, active_local=active_local,
+    # rows a combine exchange would carry back: one per kept pair, or one per (rank, token) with partials
+    seg = L.expert_offset.cpu()[torch.arange(R + 1) * cfg.El]
+    rank_of = torch.searchsorted(seg, pr.clamp(min=0).contiguous(), right=True) - 1
+    rk = torch.where(pr >= 0, rank_of, torch.full_like(rank_of, -1)).sort(dim=1).values
+    partial_rows = int((rk[:, :1] >= 0).sum().item() + ((rk[:, 1:] != rk[:, :-1]) & (rk[:, 1:] >= 0)).sum().item())
+    counts = dict(kept=kept, tokens_touched=touched, active_local=active_local, partial_rows=partial_rows,
                   bias_stride=None if inp["bias"] is None else inp["bias_stride"])
-    ab = algorithmic_bytes(cfg, C, counts, s, fp8)
+    ab = algorithmic_bytes(cfg, C, counts, s, fp8, sender)
 
     mlp_s = mlp_us_timed * 1e-6
     mlp_ai = ab["mlp_flops"] / max(ab["mlp"], 1)
@@ -367,7 +385,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "ffn": F,
                    "dest_ranks": R, "capacity": C, "routing": cfg.routing, "act_dtype": cfg.dtype,
-                   "dispatch_payload": "fp8-e4m3-block128" if fp8 else cfg.dtype},
+                   "dispatch_payload": "fp8-e4m3-block128" if fp8 else cfg.dtype,
+                   "combine": "sender-side partials" if sender else "receiver-side"},
         "roofline": roof,
         "expert_mlp_us_timed": round(mlp_us_timed, 2),
         "stages_us": {n: round(v, 2) for n, v in stage_us.items()},
@@ -379,6 +398,8 @@ def main():
         "effective_assignments_per_s": round(kept / (ms_per_step * 1e-3), 1),
         "routing": {"kept_pairs": kept, "pairs": T * k, "dropped_pairs": T * k - kept,
                     "active_local_experts": active_local},
+        "combine_link_rows": {"receiver_side": kept, "sender_side": partial_rows,
+                              "bytes_per_row": H * s},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

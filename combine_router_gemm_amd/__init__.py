@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["MOE_F32", "MOE_BF16", "MOE_FP8_BLOCK", "MoeError", "Layout", "library_path", "load_library",
            "moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_dispatch_fp8", "moe_expert_mlp_fp8",
-           "moe_rows_max", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
+           "moe_combine_send", "moe_combine_recv", "moe_rows_max", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
            "moe_expert_mlp_workspace_bytes", "moe_status_string", "EXPORTED_SYMBOLS"]
 
 MOE_F32 = 0
@@ -31,7 +31,8 @@ _LIB_NAME = "libmoe_gfx950.so"
 
 EXPORTED_SYMBOLS = ("moe_status_string", "moe_rows_max", "moe_route_workspace_bytes", "moe_route",
                     "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_expert_mlp_workspace_bytes",
-                    "moe_expert_mlp", "moe_combine", "moe_dispatch_fp8", "moe_expert_mlp_fp8")
+                    "moe_expert_mlp", "moe_combine", "moe_dispatch_fp8", "moe_expert_mlp_fp8", "moe_combine_send",
+                    "moe_combine_recv")
 
 
 class MoeError(RuntimeError):
@@ -85,6 +86,10 @@ def load_library():
     lib.moe_dispatch_fp8.restype = i32
     lib.moe_expert_mlp_fp8.argtypes = [vp, vp, ctypes.POINTER(_CLayout), vp, vp, i32, vp, vp, sz, vp]
     lib.moe_expert_mlp_fp8.restype = i32
+    lib.moe_combine_send.argtypes = [vp, i32, ctypes.POINTER(_CLayout), vp, vp, vp]
+    lib.moe_combine_send.restype = i32
+    lib.moe_combine_recv.argtypes = [vp, i32, ctypes.POINTER(_CLayout), vp, vp]
+    lib.moe_combine_recv.restype = i32
     _lib = lib
     return lib
 
@@ -275,6 +280,34 @@ def moe_combine(out_buf: torch.Tensor, layout: Layout, topk_w: torch.Tensor, y: 
         _ptr(out_buf, "out_buf"), _dtype_code(y), ctypes.byref(cl),
         _ptr(topk_w, "topk_w", torch.float32, (L.T, L.k), dev), _ptr(y, "y"), _stream(stream))
     _check(st, "moe_combine")
+
+
+def moe_combine_send(out_buf: torch.Tensor, layout: Layout, topk_w: torch.Tensor, partial: torch.Tensor,
+                     stream=None) -> None:
+    """Sender-side partial rows: partial[r, t] = sum of t's kept slots on rank r of weight times expert
+    output (fp32 accumulate, rounded once). partial is [R, T, H] in the activation type; slots of ranks
+    holding no kept slot of t are left as they are."""
+    dev = partial.device
+    L = layout
+    _ptr(out_buf, "out_buf", partial.dtype, (L.rows_max, L.H), dev)
+    _ptr(partial, "partial", shape=(L.R, L.T, L.H), device=dev)
+    cl = L.c_struct()
+    st = load_library().moe_combine_send(
+        _ptr(out_buf, "out_buf"), _dtype_code(partial), ctypes.byref(cl),
+        _ptr(topk_w, "topk_w", torch.float32, (L.T, L.k), dev), _ptr(partial, "partial"), _stream(stream))
+    _check(st, "moe_combine_send")
+
+
+def moe_combine_recv(partial: torch.Tensor, layout: Layout, y: torch.Tensor, stream=None) -> None:
+    """y[t] = sum over the ranks holding kept slots of t (ascending) of partial[r, t] (fp32, rounded once)."""
+    dev = y.device
+    L = layout
+    _ptr(partial, "partial", y.dtype, (L.R, L.T, L.H), dev)
+    _ptr(y, "y", shape=(L.T, L.H), device=dev)
+    cl = L.c_struct()
+    st = load_library().moe_combine_recv(_ptr(partial, "partial"), _dtype_code(y), ctypes.byref(cl), _ptr(y, "y"),
+                                         _stream(stream))
+    _check(st, "moe_combine_recv")
 
 
 def moe_dispatch_fp8(x: torch.Tensor, topk_ids: torch.Tensor, layout: Layout, send_q: torch.Tensor,

@@ -208,4 +208,27 @@ int moe_combine(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout
   return hip_status(moe::launch_combine(out_buf, xdt == MOE_BF16, L, topk_w, y, stream));
 }
 
+int moe_combine_send(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout, const float* topk_w,
+                     void* partial, hipStream_t stream) {
+  if (!valid_dtype(xdt)) return MOE_ERR_UNSUPPORTED;
+  const int st = check_layout(layout);
+  if (st != MOE_OK) return st;
+  const moe_layout_t& L = *layout;
+  if (L.T == 0) return MOE_OK;
+  const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
+  if (!topk_w || !partial) return MOE_ERR_INVALID;
+  if (rows > 0 && !out_buf) return MOE_ERR_INVALID;
+  return hip_status(moe::launch_combine_send(out_buf, xdt == MOE_BF16, L, topk_w, partial, stream));
+}
+
+int moe_combine_recv(const void* partial, moe_dtype_t xdt, const moe_layout_t* layout, void* y, hipStream_t stream) {
+  if (!valid_dtype(xdt)) return MOE_ERR_UNSUPPORTED;
+  const int st = check_layout(layout);
+  if (st != MOE_OK) return st;
+  const moe_layout_t& L = *layout;
+  if (L.T == 0) return MOE_OK;
+  if (!partial || !y) return MOE_ERR_INVALID;
+  return hip_status(moe::launch_combine_recv(partial, xdt == MOE_BF16, L, y, stream));
+}
+
 }  // extern "C"

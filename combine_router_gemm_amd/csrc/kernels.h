@@ -48,5 +48,9 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
 // ---- combine ----
 hipError_t launch_combine(const void* out_buf, int xdt_bf16, const moe_layout_t& L, const float* topk_w, void* y,
                           hipStream_t stream);
+// sender-side partial accumulation: partial [R, T, H] rank-major
+hipError_t launch_combine_send(const void* out_buf, int xdt_bf16, const moe_layout_t& L, const float* topk_w,
+                               void* partial, hipStream_t stream);
+hipError_t launch_combine_recv(const void* partial, int xdt_bf16, const moe_layout_t& L, void* y, hipStream_t stream);
 
 }  // namespace moe

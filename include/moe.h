@@ -192,6 +192,31 @@ int moe_combine(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout
                 const float* topk_w, void* y, hipStream_t stream);
 
 /*
+ * Combine with sender-side partial accumulation: moe_combine_send then moe_combine_recv.
+ * [EFA] "Оценка": the pages' combine accumulates only at the receiver, so one row per kept pair crosses
+ * the link; DeepEP accumulates at the sender to move fewer bytes, with a possible precision cost. Here
+ * the expert side sends one partial row per (destination rank, token) instead, and the token's side sums
+ * them. The rank of a row is the r with expert_offset[r*El] <= row < expert_offset[(r+1)*El].
+ *
+ * moe_combine_send -- for every token t and rank r holding at least one kept slot of t:
+ *   partial[r, t] = sum over those slots j, ascending, of topk_w[t,j] * out_buf[pair_row[t,j]],
+ *   accumulated in fp32 and rounded once to xdt (the extra rounding is the precision cost).
+ *   out_buf  [rows_max, H] (xdt) expert outputs, as for moe_combine
+ *   topk_w   [T, k] fp32 routing weights
+ *   partial  [R, T, H] (xdt), rank-major: what rank r returns is one contiguous block. Slots (r, t)
+ *            with no kept slot are not written.
+ * moe_combine_recv -- y[t] = sum over the ranks r holding kept slots of t, ascending, of partial[r, t],
+ *   accumulated in fp32 and rounded once; a token with every pair dropped gets y[t] = 0.
+ *   partial  as written by moe_combine_send for the same layout
+ *   y        [T, H] (xdt) output
+ * With R == 1 the result equals moe_combine's bit for bit. Both return MOE_OK at once when T == 0.
+ */
+int moe_combine_send(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout, const float* topk_w,
+                     void* partial, hipStream_t stream);
+int moe_combine_recv(const void* partial, moe_dtype_t xdt, const moe_layout_t* layout, void* y,
+                     hipStream_t stream);
+
+/*
  * fp8 block-scaled dispatch.
  * [EPM] "Dispatch": the send side packs the tokens together with their block scale factors.
  * [EFA] "Оценка": dispatch runs with fp8 block scaling, combine in bf16. The pages fix neither the fp8

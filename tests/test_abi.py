@@ -140,6 +140,22 @@ def test_mlp_and_combine_reject_invalid_arguments(lib):
     assert lib.moe_combine(FAKE, moe.MOE_BF16, ctypes.byref(_layout(E=0)), FAKE, FAKE, None) == MOE_ERR_INVALID
 
 
+def test_sender_side_combine_rejects_invalid_arguments(lib):
+    L = _layout(R=2)
+    assert lib.moe_combine_send(FAKE, moe.MOE_BF16, ctypes.byref(L), FAKE, None, None) == MOE_ERR_INVALID
+    assert lib.moe_combine_send(None, moe.MOE_BF16, ctypes.byref(L), FAKE, FAKE, None) == MOE_ERR_INVALID
+    assert lib.moe_combine_send(FAKE, moe.MOE_BF16, ctypes.byref(L), None, FAKE, None) == MOE_ERR_INVALID
+    assert lib.moe_combine_send(FAKE, 7, ctypes.byref(L), FAKE, FAKE, None) == MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine_recv(None, moe.MOE_BF16, ctypes.byref(L), FAKE, None) == MOE_ERR_INVALID
+    assert lib.moe_combine_recv(FAKE, moe.MOE_BF16, ctypes.byref(L), None, None) == MOE_ERR_INVALID
+    assert lib.moe_combine_recv(FAKE, moe.MOE_BF16, ctypes.byref(_layout(R=3)), FAKE, None) == MOE_ERR_INVALID
+    assert lib.moe_combine_recv(FAKE, moe.MOE_F32, ctypes.byref(_layout(null=("pair_row",))), FAKE, None) == \
+        MOE_ERR_INVALID
+    # no tokens: nothing to do, nothing dereferenced
+    assert lib.moe_combine_send(None, moe.MOE_BF16, ctypes.byref(_layout(T=0)), None, None, None) == 0
+    assert lib.moe_combine_recv(None, moe.MOE_BF16, ctypes.byref(_layout(T=0)), None, None) == 0
+
+
 def test_fp8_entry_points_reject_invalid_arguments(lib):
     def disp(L, xdt=moe.MOE_BF16, q=FAKE, sc=FAKE, ws=FAKE, wsb=1 << 30):
         return lib.moe_dispatch_fp8(FAKE, xdt, FAKE, ctypes.byref(L), q, sc, ws, wsb, None)
