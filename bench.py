@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default=None,
                     help="workload name or number (default: mixtral8x7b-decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--fused-combine", action="store_true",
+                    help="fuse the combine into the expert MLP's down GEMM (moe_expert_mlp_combine): the tile "
+                         "that completes a token's column band combines it at once")
     ap.add_argument("--sender-accumulate", action="store_true",
                     help="combine with sender-side partial accumulation (moe_combine_send + moe_combine_recv): "
                          "one partial row per (destination rank, token) instead of one row per kept pair")
@@ -250,6 +253,9 @@ def main():
     s = x.element_size()
     fp8 = args.fp8_dispatch
     sender = args.sender_accumulate
+    fused = args.fused_combine
+    if fused and (sender or fp8):
+        raise SystemExit("--fused-combine runs the bf16/fp32 expert MLP with the receiver-side combine only")
     if fp8 and (x.dtype != torch.bfloat16 or H % moe.MOE_FP8_BLOCK):
         raise SystemExit(f"--fp8-dispatch needs bf16 activations and H % {moe.MOE_FP8_BLOCK} == 0")
 
@@ -268,7 +274,8 @@ def main():
     xdt = moe.MOE_BF16 if x.dtype == torch.bfloat16 else moe.MOE_F32
     ws_route = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E, xdt)), dtype=torch.uint8, device=dev)
     ws_disp = torch.empty(max(1, moe.moe_dispatch_workspace_bytes(T, k, E)), dtype=torch.uint8, device=dev)
-    ws_mlp = torch.empty(max(1, moe.moe_expert_mlp_workspace_bytes(T, k, E, R, C, F, xdt)), dtype=torch.uint8,
+    ws_mlp = torch.empty(max(1, moe.moe_expert_mlp_combine_workspace_bytes(T, k, E, R, C, H, F, xdt) if fused else
+                             moe.moe_expert_mlp_workspace_bytes(T, k, E, R, C, F, xdt)), dtype=torch.uint8,
                          device=dev)
     stream = torch.cuda.current_stream()
 
@@ -289,6 +296,8 @@ def main():
             mlp_ev[0].record(stream)
         if fp8:
             moe.moe_expert_mlp_fp8(send_q, send_scale, L, inp["w_gate_up"], inp["w_down"], out_buf, workspace=ws_mlp)
+        elif fused:
+            moe.moe_expert_mlp_combine(send_buf, L, inp["w_gate_up"], inp["w_down"], wts, out_buf, y, workspace=ws_mlp)
         else:
             moe.moe_expert_mlp(send_buf, L, inp["w_gate_up"], inp["w_down"], out_buf, workspace=ws_mlp)
         if ev is not None:
@@ -298,7 +307,7 @@ def main():
         if sender:
             moe.moe_combine_send(out_buf, L, wts, partial)
             moe.moe_combine_recv(partial, L, y)
-        else:
+        elif not fused:
             moe.moe_combine(out_buf, L, wts, y)
         if ev is not None:
             ev[4].record(stream)
@@ -347,6 +356,8 @@ def main():
     counts = dict(kept=kept, tokens_touched=touched, active_local=active_local, partial_rows=partial_rows,
                   bias_stride=None if inp["bias"] is None else inp["bias_stride"])
     ab = algorithmic_bytes(cfg, C, counts, s, fp8, sender)
+    if fused:  # the combine's bytes move inside the expert-MLP call
+        ab["mlp"] += ab["combine"]
 
     mlp_s = mlp_us_timed * 1e-6
     mlp_ai = ab["mlp_flops"] / max(ab["mlp"], 1)
@@ -360,14 +371,15 @@ def main():
         achieved = ab["mlp"] / mlp_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
-    roof["traffic"] = None if fp8 else measured_traffic(cfg.name)
-    roof["kernel"] = ("moe_expert_mlp_fp8" if fp8 else "moe_expert_mlp") + \
-        " (grouped GEMM: plan + gate/up + down launches)"
+    roof["traffic"] = None if (fp8 or fused) else measured_traffic(cfg.name)
+    roof["kernel"] = ("moe_expert_mlp_fp8" if fp8 else ("moe_expert_mlp_combine" if fused else "moe_expert_mlp")) + \
+        (" (grouped GEMM: plan + counter clear + gate/up + down-with-combine launches)" if fused else
+         " (grouped GEMM: plan + gate/up + down launches)")
     roof["algorithmic_bytes"] = ab["mlp"]
     roof["algorithmic_flops"] = ab["mlp_flops"]
 
-    dc_s = (stage_us["dispatch"] + stage_us["combine"]) * 1e-6
-    dc_gbs = (ab["dispatch"] + ab["combine"]) / dc_s / 1e9
+    dc_s = (stage_us["dispatch"] + (0.0 if fused else stage_us["combine"])) * 1e-6
+    dc_gbs = (ab["dispatch"] + (0 if fused else ab["combine"])) / dc_s / 1e9
     tokens_per_s = T / (ms_per_step * 1e-3)
 
     result = {
@@ -386,13 +398,16 @@ def main():
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": k, "ffn": F,
                    "dest_ranks": R, "capacity": C, "routing": cfg.routing, "act_dtype": cfg.dtype,
                    "dispatch_payload": "fp8-e4m3-block128" if fp8 else cfg.dtype,
-                   "combine": "sender-side partials" if sender else "receiver-side"},
+                   "combine": "sender-side partials" if sender else
+                   ("fused into the down GEMM" if fused else "receiver-side")},
         "roofline": roof,
         "expert_mlp_us_timed": round(mlp_us_timed, 2),
         "stages_us": {n: round(v, 2) for n, v in stage_us.items()},
         "gpu_step_us_events": round(gpu_step_us, 2),
         "dispatch_combine": {"GB/s": round(dc_gbs, 1), "frac_hbm_peak": round(dc_gbs / HBM_PEAK_GBS, 4),
-                             "bytes": ab["dispatch"] + ab["combine"]},
+                             "bytes": ab["dispatch"] + (0 if fused else ab["combine"]),
+                             "stages": "dispatch only (the combine runs inside the expert MLP)" if fused else
+                             "dispatch + combine"},
         "route": {"TFLOP/s": round(ab["route_flops"] / (stage_us["route"] * 1e-6) / 1e12, 3),
                   "GB/s": round(ab["route"] / (stage_us["route"] * 1e-6) / 1e9, 1)},
         "effective_assignments_per_s": round(kept / (ms_per_step * 1e-3), 1),

@@ -19,7 +19,8 @@ import torch
 
 __all__ = ["MOE_F32", "MOE_BF16", "MOE_FP8_BLOCK", "MoeError", "Layout", "library_path", "load_library",
            "moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_dispatch_fp8", "moe_expert_mlp_fp8",
-           "moe_combine_send", "moe_combine_recv", "moe_rows_max", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
+           "moe_combine_send", "moe_combine_recv", "moe_expert_mlp_combine",
+           "moe_expert_mlp_combine_workspace_bytes", "moe_rows_max", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
            "moe_expert_mlp_workspace_bytes", "moe_status_string", "EXPORTED_SYMBOLS"]
 
 MOE_F32 = 0
@@ -32,7 +33,7 @@ _LIB_NAME = "libmoe_gfx950.so"
 EXPORTED_SYMBOLS = ("moe_status_string", "moe_rows_max", "moe_route_workspace_bytes", "moe_route",
                     "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_expert_mlp_workspace_bytes",
                     "moe_expert_mlp", "moe_combine", "moe_dispatch_fp8", "moe_expert_mlp_fp8", "moe_combine_send",
-                    "moe_combine_recv")
+                    "moe_combine_recv", "moe_expert_mlp_combine", "moe_expert_mlp_combine_workspace_bytes")
 
 
 class MoeError(RuntimeError):
@@ -86,6 +87,10 @@ def load_library():
     lib.moe_dispatch_fp8.restype = i32
     lib.moe_expert_mlp_fp8.argtypes = [vp, vp, ctypes.POINTER(_CLayout), vp, vp, i32, vp, vp, sz, vp]
     lib.moe_expert_mlp_fp8.restype = i32
+    lib.moe_expert_mlp_combine.argtypes = [vp, i32, ctypes.POINTER(_CLayout), vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.moe_expert_mlp_combine.restype = i32
+    lib.moe_expert_mlp_combine_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.moe_expert_mlp_combine_workspace_bytes.restype = sz
     lib.moe_combine_send.argtypes = [vp, i32, ctypes.POINTER(_CLayout), vp, vp, vp]
     lib.moe_combine_send.restype = i32
     lib.moe_combine_recv.argtypes = [vp, i32, ctypes.POINTER(_CLayout), vp, vp]
@@ -158,6 +163,10 @@ def moe_dispatch_workspace_bytes(T: int, k: int, E: int) -> int:
 
 def moe_expert_mlp_workspace_bytes(T: int, k: int, E: int, R: int, C: int, F: int, xdt: int) -> int:
     return int(load_library().moe_expert_mlp_workspace_bytes(T, k, E, R, C, F, xdt))
+
+
+def moe_expert_mlp_combine_workspace_bytes(T: int, k: int, E: int, R: int, C: int, H: int, F: int, xdt: int) -> int:
+    return int(load_library().moe_expert_mlp_combine_workspace_bytes(T, k, E, R, C, H, F, xdt))
 
 
 # ------------------------------------------------------------------------------------------------
@@ -266,6 +275,29 @@ def moe_expert_mlp(send_buf: torch.Tensor, layout: Layout, w_gate_up: torch.Tens
         _ptr(send_buf, "send_buf"), dt, ctypes.byref(cl), _ptr(w_gate_up, "w_gate_up"), _ptr(w_down, "w_down"), F,
         _ptr(out_buf, "out_buf"), _ptr(ws, "workspace"), 0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "moe_expert_mlp")
+
+
+def moe_expert_mlp_combine(send_buf: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor, w_down: torch.Tensor,
+                           topk_w: torch.Tensor, out_buf: torch.Tensor, y: torch.Tensor,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """moe_expert_mlp with moe_combine fused into its down GEMM: writes out_buf and y in one call."""
+    dev = send_buf.device
+    L = layout
+    El = L.E // L.R
+    F = w_gate_up.shape[1] // 2
+    dt = _dtype_code(send_buf)
+    _ptr(send_buf, "send_buf", shape=(L.rows_max, L.H), device=dev)
+    _ptr(w_gate_up, "w_gate_up", send_buf.dtype, (El, 2 * F, L.H), dev)
+    _ptr(w_down, "w_down", send_buf.dtype, (El, L.H, F), dev)
+    _ptr(out_buf, "out_buf", send_buf.dtype, (L.rows_max, L.H), dev)
+    _ptr(y, "y", send_buf.dtype, (L.T, L.H), dev)
+    ws = _workspace(moe_expert_mlp_combine_workspace_bytes(L.T, L.k, L.E, L.R, L.C, L.H, F, dt), workspace, dev)
+    cl = L.c_struct()
+    st = load_library().moe_expert_mlp_combine(
+        _ptr(send_buf, "send_buf"), dt, ctypes.byref(cl), _ptr(w_gate_up, "w_gate_up"), _ptr(w_down, "w_down"), F,
+        _ptr(topk_w, "topk_w", torch.float32, (L.T, L.k), dev), _ptr(out_buf, "out_buf"), _ptr(y, "y"),
+        _ptr(ws, "workspace"), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(st, "moe_expert_mlp_combine")
 
 
 def moe_combine(out_buf: torch.Tensor, layout: Layout, topk_w: torch.Tensor, y: torch.Tensor,

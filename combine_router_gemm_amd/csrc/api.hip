@@ -123,11 +123,27 @@ size_t moe_expert_mlp_workspace_bytes(int T, int k, int E, int R, int C, int F, 
 }
 
 namespace {
-// Shared by moe_expert_mlp and moe_expert_mlp_fp8: validation, workspace carving, launch. a_scale !=
-// nullptr means send_buf holds E4M3 codes with these block scales.
+// counters of the fused combine: one per (token, down-GEMM column band)
+size_t combine_counter_bytes(int T, int k, int E, int R, int C, int H, int F, moe_dtype_t xdt) {
+  const int64_t rows = moe_rows_max(T, k, E, C);
+  const moe::MlpTiles tiles = moe::mlp_pick_tiles(rows, E / R, H, F, xdt == MOE_BF16);
+  const int64_t bands = (H + moe::mlp_down_cols(tiles) - 1) / moe::mlp_down_cols(tiles);
+  return moe::align256((size_t)((int64_t)T * bands) * sizeof(int));
+}
+}  // namespace
+
+size_t moe_expert_mlp_combine_workspace_bytes(int T, int k, int E, int R, int C, int H, int F, moe_dtype_t xdt) {
+  if (E <= 0 || R <= 0 || E % R != 0 || F <= 0 || H <= 0 || T < 0) return 0;
+  return moe_expert_mlp_workspace_bytes(T, k, E, R, C, F, xdt) + combine_counter_bytes(T, k, E, R, C, H, F, xdt);
+}
+
+namespace {
+// Shared by moe_expert_mlp, moe_expert_mlp_fp8 and moe_expert_mlp_combine: validation, workspace carving,
+// launch. a_scale != nullptr means send_buf holds E4M3 codes with these block scales; y != nullptr fuses
+// the combine into the down GEMM.
 int expert_mlp(const void* send_buf, const float* a_scale, moe_dtype_t xdt, const moe_layout_t* layout,
                const void* w_gate_up, const void* w_down, int F, void* out_buf, void* workspace,
-               size_t workspace_bytes, hipStream_t stream) {
+               size_t workspace_bytes, hipStream_t stream, const float* topk_w = nullptr, void* y = nullptr) {
   if (!valid_dtype(xdt)) return MOE_ERR_UNSUPPORTED;
   const int st = check_layout(layout);
   if (st != MOE_OK) return st;
@@ -138,7 +154,8 @@ int expert_mlp(const void* send_buf, const float* a_scale, moe_dtype_t xdt, cons
   const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
   if (!w_gate_up || !w_down) return MOE_ERR_INVALID;
   if (rows > 0 && (!send_buf || !out_buf)) return MOE_ERR_INVALID;
-  const size_t need = moe_expert_mlp_workspace_bytes(L.T, L.k, L.E, L.R, L.C, F, xdt);
+  const size_t need = y ? moe_expert_mlp_combine_workspace_bytes(L.T, L.k, L.E, L.R, L.C, L.H, F, xdt)
+                        : moe_expert_mlp_workspace_bytes(L.T, L.k, L.E, L.R, L.C, F, xdt);
   if (!workspace || workspace_bytes < need) return MOE_ERR_INVALID;
   const int El = L.E / L.R;
   char* ws = static_cast<char*>(workspace);
@@ -147,9 +164,11 @@ int expert_mlp(const void* send_buf, const float* a_scale, moe_dtype_t xdt, cons
   int* perm = reinterpret_cast<int*>(ws);
   ws += moe::align256((size_t)rows * sizeof(int));
   void* hbuf = ws;
+  ws += moe::align256((size_t)rows * (size_t)F * (xdt == MOE_BF16 ? 2 : 4));
+  int* counter = y ? reinterpret_cast<int*>(ws) : nullptr;
   const moe::MlpTiles tiles = moe::mlp_pick_tiles(rows, El, L.H, F, xdt == MOE_BF16);
   return hip_status(moe::launch_expert_mlp(send_buf, xdt == MOE_BF16, L, w_gate_up, w_down, F, out_buf, plan, perm,
-                                           hbuf, tiles, device_cus(), stream, a_scale));
+                                           hbuf, tiles, device_cus(), stream, a_scale, topk_w, y, counter));
 }
 
 }  // namespace
@@ -159,6 +178,20 @@ int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* la
                    hipStream_t stream) {
   return expert_mlp(send_buf, nullptr, xdt, layout, w_gate_up, w_down, F, out_buf, workspace, workspace_bytes,
                     stream);
+}
+
+int moe_expert_mlp_combine(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* layout, const void* w_gate_up,
+                           const void* w_down, int F, const float* topk_w, void* out_buf, void* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_layout(layout);
+  if (st != MOE_OK) return st;
+  if (layout->T > 0 && (!topk_w || !y)) return MOE_ERR_INVALID;
+  if (layout->T == 0) {  // nothing to combine: the plain expert MLP (its plan kernel only)
+    return expert_mlp(send_buf, nullptr, xdt, layout, w_gate_up, w_down, F, out_buf, workspace, workspace_bytes,
+                      stream);
+  }
+  return expert_mlp(send_buf, nullptr, xdt, layout, w_gate_up, w_down, F, out_buf, workspace, workspace_bytes,
+                    stream, topk_w, y);
 }
 
 int moe_dispatch_fp8(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const moe_layout_t* layout,

@@ -41,9 +41,13 @@ MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16);
 size_t mlp_plan_ints(int El);
 // a_scale != nullptr: send_buf holds E4M3 codes with these block scales; they are expanded to bf16 in
 // out_buf first and the bf16 GEMMs read them from there
+// y != nullptr: the combine is fused into the down GEMM (y [T, H], counter [T, ceil(H / mlp_down_cols)])
 hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
                              const void* w_down, int F, void* out_buf, int* plan, int* perm, void* hbuf,
-                             const MlpTiles& tiles, int num_cus, hipStream_t stream, const float* a_scale);
+                             const MlpTiles& tiles, int num_cus, hipStream_t stream, const float* a_scale,
+                             const float* topk_w = nullptr, void* y = nullptr, int* counter = nullptr);
+// columns per down-GEMM tile (the band of the fused combine's counters)
+int mlp_down_cols(const MlpTiles& tiles);
 
 // ---- combine ----
 hipError_t launch_combine(const void* out_buf, int xdt_bf16, const moe_layout_t& L, const float* topk_w, void* y,

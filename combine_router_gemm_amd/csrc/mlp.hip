@@ -162,6 +162,14 @@ struct GemmArgs {
   int a_bytes;          // bytes of A (rows_max x lda elements) when it fits 31-bit buffer offsets, else 0
   int w_bytes;          // bytes of one expert's weights (w_stride elements), same rule
   int k_rotate;         // start each tile's K loop at a tile-dependent stage (see k_rotation)
+  // down GEMM with the combine fused in (see tile_arrive_combine); unused otherwise
+  const int* row_token;  // [rows] token of each send row
+  const int* pair_row;   // [T, k] send row of each (token, slot), -1 if dropped
+  const float* topk_w;   // [T, k] routing weights
+  int* counter;          // [T, column bands] rows of the token finished per band (zeroed before the GEMM)
+  void* y;               // [T, N] combine output
+  int k;
+  int out_bytes;         // bytes of Out when 31-bit buffer offsets cover it, else 0
 };
 
 // Eight OCP E4M3 codes (q.x, q.y, little-endian bytes) times their block scale sc (a power of two) as
@@ -224,13 +232,130 @@ __device__ __forceinline__ int k_rotation(int on, int l, int n_tiles, int nt, in
 }
 inline int k_rotate_for(int K, int elem_bytes) { return MOE_K_ROTATE && ((int64_t)K * elem_bytes) % 8192 == 0; }
 
+// ---- the combine fused into the down GEMM ----
+// Expert-output rows that another tile combines travel through agent-scope (sc1) loads and stores: they
+// are coherent across the XCDs' L2 caches by themselves, so no cache-wide writeback or invalidate is
+// needed, and the L2 keeps the operands the other workgroups are reusing.
+__device__ __forceinline__ void st16_agent(void* p, u32x4 v) {
+  uint64_t* q = static_cast<uint64_t*>(p);
+  __hip_atomic_store(q, ((uint64_t)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, ((uint64_t)v.w << 32) | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 ld16_agent(const void* p) {
+  const uint64_t* q = static_cast<const uint64_t*>(p);
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+}
+// 16-byte agent-scope (sc1) buffer accesses, where the buffer fits 31-bit offsets
+__device__ __forceinline__ u32x4 ld16_agent(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
+}
+__device__ __forceinline__ void st16_agent(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16);
+}
+__device__ __forceinline__ void st_agent(bf16_t* p, float v) {
+  const bf16_t h = (bf16_t)v;
+  __hip_atomic_store(reinterpret_cast<uint16_t*>(p), __builtin_bit_cast(uint16_t, h), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Tile-level overlap of the grouped GEMM with the combine: once a down-GEMM tile has stored its rows
+// (columns [n0, n0 + OUT_COLS) of some tokens' expert outputs), it counts them per (token, column band).
+// The tile that brings a token's count to its number of kept slots holds the last missing piece of that
+// band, and combines it at once: y[t, band] = sum over kept slots j, ascending, of w[t, j] * out[row_j],
+// fp32, rounded once (the combine's own arithmetic, so the result equals moe_combine's bit for bit).
+// The combine of early bands thus runs while later tiles are still being computed. Nothing ever waits:
+// a workgroup either finishes a band or leaves it to the tile that will. The tile's rows were stored at
+// agent scope; every thread waits for its stores to complete before the workgroup counts them, and the
+// tile that completes a band reads the other tiles' rows at agent scope after its count returned.
+// LDS: s_list holds at least BM + 1 ints and is free on entry.
+template <typename T, int NTH, int OUT_COLS>
+__device__ __forceinline__ void tile_arrive_combine(const GemmArgs& a, int p0, int m_rows, int n0, int nt,
+                                                    int n_bands, int* s_list) {
+  constexpr int VN = Vec<T>::N;
+  const int tid = threadIdx.x;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's rows have reached the coherent level
+  if (tid == 0) s_list[0] = 0;
+  __syncthreads();
+  for (int r = tid; r < m_rows; r += NTH) {
+    const int p = p0 + r;
+    const int orow = a.out_perm ? a.out_perm[p] : p;
+    const int t = a.row_token[orow];
+    int kept = 0;
+    for (int j = 0; j < a.k; ++j) kept += a.pair_row[(int64_t)t * a.k + j] >= 0 ? 1 : 0;
+    const int old = atomicAdd(&a.counter[(int64_t)t * n_bands + nt], 1);
+    if (old == kept - 1) s_list[1 + atomicAdd(&s_list[0], 1)] = t;
+  }
+  __syncthreads();
+  const int n = s_list[0];
+  if (n > 0) {
+    const T* out = static_cast<const T*>(a.Out);
+    const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(a.Out, (short)0, a.out_bytes, 0x00020000);
+    T* y = static_cast<T*>(a.y);
+    const int cpb = (min(OUT_COLS, a.N - n0) + VN - 1) / VN;  // 16-byte chunks of the band (N % VN == 0)
+    for (int idx = tid; idx < n * cpb; idx += NTH) {
+      const int t = s_list[1 + idx / cpb];
+      const int col = n0 + (idx % cpb) * VN;
+      // all k rows in flight at once, then the sum in slot order
+      int rows[MOE_MAX_TOPK];
+      u32x4 raw[MOE_MAX_TOPK];
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j) rows[j] = j < a.k ? a.pair_row[(int64_t)t * a.k + j] : -1;
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j)
+        raw[j] = rows[j] < 0 ? u32x4{0u, 0u, 0u, 0u}
+                 : a.out_bytes > 0 ? ld16_agent(out_rsrc, (rows[j] * a.ldo + col) * (int)sizeof(T))
+                                   : ld16_agent(out + (int64_t)rows[j] * a.ldo + col);
+      float acc[VN];
+#pragma unroll
+      for (int q = 0; q < VN; ++q) acc[q] = 0.f;
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        if (rows[j] >= 0) {
+          const float w = a.topk_w[(int64_t)t * a.k + j];
+          float val[VN];
+          unpack(raw[j], val);
+#pragma unroll
+          for (int q = 0; q < VN; ++q) acc[q] = fmaf(w, val[q], acc[q]);
+        }
+      }
+      st16(y + (int64_t)t * a.N + col, pack(acc));
+    }
+  }
+  __syncthreads();  // s_list is free again before the next tile reuses the buffers
+}
+
+// Before a GEMM with the fused combine: zero the per-(token, band) counters, and write y = 0 for the
+// tokens with no kept slot (no tile ever completes them). One thread per counter / per 16-byte chunk.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_prep_kernel(const int* __restrict__ pair_row, int T_, int k, int H,
+                                                           int n_bands, int* __restrict__ counter,
+                                                           T* __restrict__ y) {
+  constexpr int VN = Vec<T>::N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t ncnt = (int64_t)T_ * n_bands;
+  if (i < ncnt) counter[i] = 0;
+  const int cpr = H / VN;
+  if (i < (int64_t)T_ * cpr) {
+    const int t = (int)(i / cpr);
+    bool any = false;
+    for (int j = 0; j < k; ++j) any = any || pair_row[(int64_t)t * k + j] >= 0;
+    if (!any) st16(y + (int64_t)t * H + (i % cpr) * VN, u32x4{0u, 0u, 0u, 0u});
+  }
+}
+
 // BM x BN tile, BK-deep LDS stages, WM x WN waves, MFMA op Op. GATED: the B tile holds BN/2 gate rows
 // then the BN/2 up rows of the same output columns, and each wave owns matching gate and up
 // accumulators.
 template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
-          bool BUF>
+          bool BUF, bool COMBINE = false>
 __global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(MOE_GEMM_MIN_WAVES)))
 void mlp_gemm_kernel(GemmArgs args) {
+  static_assert(!COMBINE || !GATED, "the combine follows the down GEMM");
   constexpr int NTH = WM * WN * 64;
   constexpr int VN = Vec<T>::N;           // elements per 16-byte vector
   constexpr int PAD = 16 / sizeof(T);     // one vector of padding per LDS row
@@ -486,10 +611,16 @@ void mlp_gemm_kernel(GemmArgs args) {
             else v = acc[i][j][q];
             const int p = p0 + row;
             const int orow = args.out_perm ? args.out_perm[p] : p;
-            Out[(int64_t)orow * args.ldo + col] = from_f32<T>(v);
+            if (COMBINE) st_agent(Out + (int64_t)orow * args.ldo + col, v);
+            else Out[(int64_t)orow * args.ldo + col] = from_f32<T>(v);
           }
         }
       }
+    }
+    if (COMBINE) {
+      static_assert(BM * LDR * sizeof(T) >= (BM + 1) * sizeof(int), "token list must fit the A stage");
+      if (LDB == 2) lds_barrier();  // the last stage's fragments are read before As is reused
+      tile_arrive_combine<T, NTH, OUT_COLS>(args, p0, m_rows, n0, nt, n_tiles, reinterpret_cast<int*>(&As[0][0]));
     }
   }
 }
@@ -518,8 +649,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool GATED, int NS, int SWZ, bool SPREAD>
+template <int BM, int BN, int BK, int WM, int WN, bool GATED, int NS, int SWZ, bool SPREAD, bool COMBINE = false>
 __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args, int a_bytes) {
+  static_assert(!COMBINE || !GATED, "the combine follows the down GEMM");
   using Op = Op32;
   static_assert(BK == 32 || BK == 64, "32- or 64-deep stages");
   constexpr int S = 32, ROWB = BK * 2;
@@ -724,24 +856,33 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
       }
     }
     lds_barrier();
+    // with the fused combine, Out (below 2 GiB here, like every operand of this kernel) is stored at agent scope
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Out, (short)0, COMBINE ? args.out_bytes : 0, 0x00020000);
     for (int idx = tid; idx < BM * CPO; idx += NW * 64) {
       const int row = idx / CPO, ch = idx % CPO;
       const int col = n0 + ch * 8;
       if (row < m_rows && col < args.N) {
         const int p = p0 + row;
         const int orow = args.out_perm ? args.out_perm[p] : p;
-        st16(Out + (int64_t)orow * args.ldo + col, ld16(smem + out_off(row, ch * 8)));
+        if (COMBINE) st16_agent(out_rsrc, (orow * args.ldo + col) * 2, ld16(smem + out_off(row, ch * 8)));
+        else st16(Out + (int64_t)orow * args.ldo + col, ld16(smem + out_off(row, ch * 8)));
       }
+    }
+    if (COMBINE) {
+      lds_barrier();  // every wave has read its output chunks before the token list overwrites them
+      tile_arrive_combine<bf16_t, NW * 64, OUT_COLS>(args, p0, m_rows, n0, nt, n_tiles, reinterpret_cast<int*>(smem));
     }
   }
 }
 
-template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT>
+template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
+          bool COMBINE = false>
 void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
   if (a.a_bytes > 0 && a.w_bytes > 0)
-    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, true><<<grid, WM * WN * 64, 0, stream>>>(a);
+    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, true, COMBINE><<<grid, WM * WN * 64, 0, stream>>>(a);
   else
-    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, false><<<grid, WM * WN * 64, 0, stream>>>(a);
+    mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, false, COMBINE><<<grid, WM * WN * 64, 0, stream>>>(a);
 }
 
 // Persistent grid sizes in workgroups per CU and the compute-bound tile shapes; overridable at compile
@@ -889,18 +1030,18 @@ bool dl_fits(int64_t rows_max, int H, int F) {
          wgu_bytes < lim && wdn_bytes < lim;
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool SPREAD>
+template <int BM, int BN, int WM, int WN, int NS, bool SPREAD, bool COMBINE>
 void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
                int64_t h_bytes, int num_cus, hipStream_t stream) {
   const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, BN / 2), num_cus, MOE_DL_WPC);
   mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, true, NS, MOE_DL_SWZ, SPREAD><<<g1, WM * WN * 64, 0, stream>>>(
       gu, (int)send_bytes);
   const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, BN), num_cus, MOE_DL_WPC);
-  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, false, NS, MOE_DL_SWZ, SPREAD><<<g2, WM * WN * 64, 0, stream>>>(
+  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, false, NS, MOE_DL_SWZ, SPREAD, COMBINE><<<g2, WM * WN * 64, 0, stream>>>(
       dn, (int)h_bytes);
 }
 
-template <int BM>
+template <int BM, bool COMBINE>
 void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int El, int num_cus,
                    hipStream_t stream) {
   // with many local experts of few rows each, streaming (non-temporal) weight loads in the gate/up
@@ -913,8 +1054,8 @@ void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, i
     launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, false>(
         gu, g1, stream);
   const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
-  launch_gemm<bf16_t, Op16, BM, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB, false>(
-      dn, g2, stream);
+  launch_gemm<bf16_t, Op16, BM, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB, false,
+              COMBINE>(dn, g2, stream);
 }
 }  // namespace
 
@@ -930,9 +1071,60 @@ MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16) {
   return MlpTiles{128, 3};
 }
 
+int mlp_down_cols(const MlpTiles& tiles) {
+  switch (tiles.variant) {
+    case 3: return MOE_DL_BN;
+    case 4: return MOE_DLT_BN;
+    case 0: return MOE_PRE_BN;
+    case 1:
+    case 5: return MOE_DEC_DN_BN;
+    default: return 64;  // fp32
+  }
+}
+
+namespace {
+template <bool COMBINE>
+void launch_gemms(const GemmArgs& gu, const GemmArgs& dn, const MlpTiles& tiles, int64_t max_mtiles, int64_t rows_max,
+                  int H, int F, int El, int num_cus, hipStream_t stream) {
+  switch (tiles.variant) {
+    case 3:
+      launch_dl<128, MOE_DL_BN, MOE_DL_WM, MOE_DL_WN, MOE_DL_NS, MOE_DL_SPREAD, COMBINE>(
+          gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
+      break;
+    case 4:
+      launch_dl<256, MOE_DLT_BN, MOE_DLT_WM, MOE_DLT_WN, MOE_DLT_NS, MOE_DLT_SPREAD, COMBINE>(
+          gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
+      break;
+    case 0: {  // bf16, many rows per expert, operands staged through registers
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_PRE_BN / 2), num_cus, MOE_PRE_WPC);
+      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS,
+                  MOE_PRE_LDB, false>(gu, g1, stream);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_PRE_BN), num_cus, MOE_PRE_WPC);
+      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, false, MOE_PRE_RS,
+                  MOE_PRE_LDB, false, COMBINE>(dn, g2, stream);
+      break;
+    }
+    case 1:  // bf16, few rows per expert: stream the weights through 32- or 64-row tiles
+      launch_decode<32, COMBINE>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
+      break;
+    case 5:
+      launch_decode<64, COMBINE>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
+      break;
+    default: {  // fp32
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus, 2);
+      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, true, 2, 2, false>(gu, g1, stream);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 64), num_cus, 2);
+      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, false, 2, 2, false, COMBINE>(dn, g2, stream);
+      break;
+    }
+  }
+}
+}  // namespace
+
 hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layout_t& L, const void* w_gate_up,
                              const void* w_down, int F, void* out_buf, int* plan, int* perm, void* hbuf,
-                             const MlpTiles& tiles, int num_cus, hipStream_t stream, const float* a_scale) {
+                             const MlpTiles& tiles, int num_cus, hipStream_t stream, const float* a_scale,
+                             const float* topk_w, void* y, int* counter) {
   if (a_scale != nullptr && moe_rows_max(L.T, L.k, L.E, L.C) > 0) {
     // fp8 rows: expand them to bf16 in out_buf (rows_max x H bf16, unused until the down GEMM writes it in
     // a later launch) and run the bf16 GEMMs on them. Decoding inside the gate/up GEMM instead (codes
@@ -989,35 +1181,30 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   dn.w_bytes = buffer_bytes(dn.w_stride * (xdt_bf16 ? 2 : 4));
   dn.k_rotate = k_rotate_for(F, xdt_bf16 ? 2 : 4);
 
-  switch (tiles.variant) {
-    case 3:
-      launch_dl<128, MOE_DL_BN, MOE_DL_WM, MOE_DL_WN, MOE_DL_NS, MOE_DL_SPREAD>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
-                                                                 rows_max * (int64_t)F * 2, num_cus, stream);
-      break;
-    case 4:
-      launch_dl<256, MOE_DLT_BN, MOE_DLT_WM, MOE_DLT_WN, MOE_DLT_NS, MOE_DLT_SPREAD>(
-          gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
-      break;
-    case 0: {  // bf16, many rows per expert, operands staged through registers
-      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_PRE_BN / 2), num_cus, MOE_PRE_WPC);
-      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS, MOE_PRE_LDB, false>(gu, g1, stream);
-      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_PRE_BN), num_cus, MOE_PRE_WPC);
-      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, false, MOE_PRE_RS, MOE_PRE_LDB, false>(dn, g2, stream);
-      break;
+  if (y != nullptr) {
+    // the combine fused into the down GEMM: counters zeroed and the y rows of tokens with no kept slot
+    // cleared first
+    const int n_bands = ceil_div_host(H, mlp_down_cols(tiles));
+    dn.row_token = L.row_token;
+    dn.pair_row = L.pair_row;
+    dn.topk_w = topk_w;
+    dn.counter = counter;
+    dn.y = y;
+    dn.k = L.k;
+    dn.out_bytes = buffer_bytes(rows_max * H * (xdt_bf16 ? 2 : 4));
+    const int64_t work = std::max<int64_t>((int64_t)L.T * n_bands, (int64_t)L.T * (H / (xdt_bf16 ? 8 : 4)));
+    if (work > 0) {
+      const unsigned g = (unsigned)ceil_div_host64(work, 256);
+      if (xdt_bf16)
+        combine_prep_kernel<bf16_t><<<g, 256, 0, stream>>>(L.pair_row, L.T, L.k, H, n_bands, counter,
+                                                           static_cast<bf16_t*>(y));
+      else
+        combine_prep_kernel<float><<<g, 256, 0, stream>>>(L.pair_row, L.T, L.k, H, n_bands, counter,
+                                                          static_cast<float*>(y));
     }
-    case 1:  // bf16, few rows per expert: stream the weights through 32- or 64-row tiles
-      launch_decode<32>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
-      break;
-    case 5:
-      launch_decode<64>(gu, dn, max_mtiles, H, F, El, num_cus, stream);
-      break;
-    default: {  // fp32
-      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, 32), num_cus, 2);
-      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, true, 2, 2, false>(gu, g1, stream);
-      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, 64), num_cus, 2);
-      launch_gemm<float, OpF32, 32, 64, 32, 1, 2, false, 2, 2, false>(dn, g2, stream);
-      break;
-    }
+    launch_gemms<true>(gu, dn, tiles, max_mtiles, rows_max, H, F, El, num_cus, stream);
+  } else {
+    launch_gemms<false>(gu, dn, tiles, max_mtiles, rows_max, H, F, El, num_cus, stream);
   }
   return hipGetLastError();
 }

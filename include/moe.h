@@ -192,6 +192,29 @@ int moe_combine(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout
                 const float* topk_w, void* y, hipStream_t stream);
 
 /*
+ * moe_expert_mlp_combine -- moe_expert_mlp with moe_combine fused into its down GEMM: one call writes
+ * out_buf and y.
+ * [OVL] "tile-level signalling": the GEMM epilogue publishes per-tile readiness and the consumer starts
+ * on a segment as soon as the tiles it needs are done, instead of after the whole GEMM. Here every
+ * down-GEMM tile, once it has stored its rows, counts them per (token, column band); the tile that
+ * completes a token's band computes that band of y at once, so the combine of early bands overlaps the
+ * tiles still running. No workgroup ever waits for another.
+ *   y[t] = sum over kept slots j, ascending, of topk_w[t,j] * out_buf[pair_row[t,j]], accumulated in
+ *   fp32 and rounded once; equal bit for bit to moe_expert_mlp followed by moe_combine.
+ *   send_buf, layout, w_gate_up, w_down, F, out_buf  as for moe_expert_mlp
+ *   topk_w     [T, k] fp32 routing weights
+ *   y          [T, H] (xdt) output
+ *   workspace  device scratch of at least moe_expert_mlp_combine_workspace_bytes(T, k, E, R, C, H, F, xdt)
+ *              bytes: the expert-MLP scratch plus one int per (token, column band), cleared by the call
+ * Calls that overlap on one stream or device must use separate workspaces.
+ */
+size_t moe_expert_mlp_combine_workspace_bytes(int T, int k, int E, int R, int C, int H, int F, moe_dtype_t xdt);
+int moe_expert_mlp_combine(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* layout,
+                           const void* w_gate_up, const void* w_down, int F, const float* topk_w,
+                           void* out_buf, void* y, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/*
  * Combine with sender-side partial accumulation: moe_combine_send then moe_combine_recv.
  * [EFA] "Оценка": the pages' combine accumulates only at the receiver, so one row per kept pair crosses
  * the link; DeepEP accumulates at the sender to move fewer bytes, with a possible precision cost. Here

@@ -140,6 +140,24 @@ def test_mlp_and_combine_reject_invalid_arguments(lib):
     assert lib.moe_combine(FAKE, moe.MOE_BF16, ctypes.byref(_layout(E=0)), FAKE, FAKE, None) == MOE_ERR_INVALID
 
 
+def test_fused_combine_rejects_invalid_arguments_and_sizes_its_workspace(lib):
+    L = _layout(T=16, k=2, E=8, R=1, C=4, H=64)
+    base = lib.moe_expert_mlp_workspace_bytes(16, 2, 8, 1, 4, 64, moe.MOE_BF16)
+    fused = lib.moe_expert_mlp_combine_workspace_bytes(16, 2, 8, 1, 4, 64, 64, moe.MOE_BF16)
+    assert fused > base                          # plus one counter per (token, column band)
+    assert lib.moe_expert_mlp_combine_workspace_bytes(16, 2, 8, 3, 4, 64, 64, moe.MOE_BF16) == 0  # E % R != 0
+
+    def call(L, topk_w=FAKE, y=FAKE, ws=FAKE, wsb=1 << 30, F=64):
+        return lib.moe_expert_mlp_combine(FAKE, moe.MOE_BF16, ctypes.byref(L), FAKE, FAKE, F, topk_w, FAKE, y, ws,
+                                          wsb, None)
+    assert call(L, topk_w=None) == MOE_ERR_INVALID
+    assert call(L, y=None) == MOE_ERR_INVALID
+    assert call(L, ws=None) == MOE_ERR_INVALID
+    assert call(L, wsb=base) == MOE_ERR_INVALID   # the plain expert-MLP workspace is too small
+    assert call(L, F=12) == MOE_ERR_UNSUPPORTED
+    assert call(_layout(R=3)) == MOE_ERR_INVALID
+
+
 def test_sender_side_combine_rejects_invalid_arguments(lib):
     L = _layout(R=2)
     assert lib.moe_combine_send(FAKE, moe.MOE_BF16, ctypes.byref(L), FAKE, None, None) == MOE_ERR_INVALID
