@@ -236,11 +236,6 @@ inline int k_rotate_for(int K, int elem_bytes) { return MOE_K_ROTATE && ((int64_
 // Expert-output rows that another tile combines travel through agent-scope (sc1) loads and stores: they
 // are coherent across the XCDs' L2 caches by themselves, so no cache-wide writeback or invalidate is
 // needed, and the L2 keeps the operands the other workgroups are reusing.
-__device__ __forceinline__ void st16_agent(void* p, u32x4 v) {
-  uint64_t* q = static_cast<uint64_t*>(p);
-  __hip_atomic_store(q, ((uint64_t)v.y << 32) | v.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, ((uint64_t)v.w << 32) | v.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ u32x4 ld16_agent(const void* p) {
   const uint64_t* q = static_cast<const uint64_t*>(p);
   const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
