@@ -30,6 +30,11 @@
 //                         the LDS bit), NS LDS stages in flight, 128- or 256-row tiles on
 //                         v_mfma_f32_32x32x16_bf16, epilogue staged through LDS.
 //   All accumulate in fp32.
+//   fp8_rows_to_bf16  fp8 block-scaled send rows (E4M3 codes + power-of-two scales) expanded to bf16 in
+//                     out_buf before the GEMMs, which then read them like bf16 rows.
+//   COMBINE           the down pass of either family with the combine fused in: each tile counts its
+//                     rows per (token, column band) and the tile completing a band combines it
+//                     (tile_arrive_combine; combine_prep clears the counters first).
 #include "common.h"
 #include "kernels.h"
 #include "mfma.h"
