@@ -265,6 +265,12 @@ def test_edge_cases(name, T, H, E, k, F, R, C, dtype, routing):
     inp["C"] = C
     print(f"\n[gpu] edge case {name}", flush=True)
     out = run_layer(inp, k, R)
+    check_layer_full(cfg, inp, out, T, E, k, F, R, C)
+
+
+def check_layer_full(cfg, inp, out, T, E, k, F, R, C):
+    """Every stage of a small layer against the whole oracle (route on the GPU logits, dispatch and send
+    rows bit-exact, expert MLP, combine and the layer within the activation type's tolerance)."""
     if T == 0:
         L = out["layout"]
         assert np.all(to_np(L.expert_count) == 0) and np.all(to_np(L.expert_offset) == 0)

@@ -5,8 +5,10 @@ through the C ABI, on the GPU's own dispatch layout and expert outputs.
            normwise) of the oracle's; absent slots keep the sentinel the buffer was filled with
   y        within the same tolerance of the oracle's receive side on the oracle's partials
   R = 1    y equals moe_combine's output bit for bit (one partial per token, summed in the same order)
-  any R    |y_send - y_combine| <= u * (sum over ranks of |partial| + |y_send| + |y_combine|), u the unit
-           roundoff of the activation type: each partial adds one rounding
+  any R    |y_send - y_combine| <= u * (sum over ranks of |partial| + |y_send| + |y_combine|)
+                                    + (k + R + 2) * 2^-24 * sum over kept slots of |w * row|,
+           u the unit roundoff of the activation type: each partial adds one rounding, and both sides sum
+           in fp32 (one fp32 rounding per addition; negligible for bf16, the same order as u for fp32)
 The full-size workloads are checked on every token where T <= 4096 (configs 1-4) and on 512 sampled
 tokens for config 5; the edge shapes in full.
 """
@@ -76,7 +78,13 @@ def _check(cfg_E, R, out, partial, y, tokens):
     mag = np.zeros_like(got_y)
     for r in range(R):
         mag[present[r]] += np.abs(f(got_p[r][present[r]], dt))
-    bound = UNIT[dt] * (mag + np.abs(got_y) + np.abs(y_comb)) + 1e-30
+    terms = np.zeros_like(got_y)  # sum over kept slots of |w * row|
+    obf = np.abs(f(ob, dt))
+    for j in range(pr_local.shape[1]):
+        m = pr_local[:, j] >= 0
+        terms[m] += np.abs(w[m, j:j + 1].astype(np.float64)) * obf[pr_local[m, j]]
+    k = pr_local.shape[1]
+    bound = UNIT[dt] * (mag + np.abs(got_y) + np.abs(y_comb)) + (k + R + 2) * 2.0 ** -24 * terms + 1e-30
     assert np.all(np.abs(got_y - y_comb) <= bound)
     assert np.all(got_y[(pr < 0).all(axis=1)] == 0.0)
     if R == 1:
