@@ -233,8 +233,11 @@ __global__ __launch_bounds__(256) void fp8_rows_to_bf16_kernel(const uint8_t* __
 // starting stage recovers it (the 28 KB rows of Mixtral's down weights: 3-4 % faster). Tiles that share
 // weights (the M tiles of one expert and N tile) get the same rotation, so they keep sharing them
 // through L2.
+#ifndef MOE_K_ROT_STRIDE
+#define MOE_K_ROT_STRIDE 7
+#endif
 __device__ __forceinline__ int k_rotation(int on, int l, int n_tiles, int nt, int nk) {
-  return on ? (int)(((int64_t)l * n_tiles + nt) * 7 % nk) : 0;
+  return on ? (int)(((int64_t)l * n_tiles + nt) * MOE_K_ROT_STRIDE % nk) : 0;
 }
 inline int k_rotate_for(int K, int elem_bytes) { return MOE_K_ROTATE && ((int64_t)K * elem_bytes) % 4096 == 0; }
 
