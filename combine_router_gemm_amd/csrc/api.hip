@@ -26,6 +26,11 @@ constexpr int ROUTE_PLAN_CUS = 256;
 
 bool valid_dtype(moe_dtype_t d) { return d == MOE_F32 || d == MOE_BF16; }
 
+// the kernels move activations, weights and rows in 16-byte vectors and int / fp32 arrays in 4-byte words
+// (a null pointer passes: the null checks come first)
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 int check_layout(const moe_layout_t* L) {
   if (!L) return MOE_ERR_INVALID;
   if (L->T < 0 || L->C < 0 || L->E < 1 || L->R < 1 || L->k < 1 || L->H < 1) return MOE_ERR_INVALID;
@@ -37,6 +42,9 @@ int check_layout(const moe_layout_t* L) {
   const int64_t rows = moe_rows_max(L->T, L->k, L->E, L->C);
   if (rows > 0 && (!L->row_token || !L->row_slot)) return MOE_ERR_INVALID;
   if (L->T > 0 && !L->pair_row) return MOE_ERR_INVALID;
+  if (!al4(L->expert_count) || !al4(L->expert_kept) || !al4(L->expert_overflow) || !al4(L->expert_offset) ||
+      !al4(L->row_token) || !al4(L->row_slot) || !al4(L->pair_row))
+    return MOE_ERR_INVALID;
   return MOE_OK;
 }
 
@@ -81,6 +89,9 @@ int moe_route(const void* x, moe_dtype_t xdt, const float* w_router, const float
   if ((int64_t)T * E > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !logits || !topk_ids || !topk_w) return MOE_ERR_INVALID;
+  if (!al16(x) || !al16(w_router) || !al16(workspace) || !al4(logit_bias) || !al4(logits) || !al4(topk_ids) ||
+      !al4(topk_w))
+    return MOE_ERR_INVALID;
   const size_t need = moe_route_workspace_bytes(T, H, E, xdt);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_INVALID;
   const int splits = moe::route_splits(T, H, E, xdt == MOE_BF16, ROUTE_PLAN_CUS);
@@ -104,6 +115,7 @@ int moe_dispatch(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const 
   const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
   if (L.T > 0 && (!x || !topk_ids)) return MOE_ERR_INVALID;
   if (rows > 0 && !send_buf) return MOE_ERR_INVALID;
+  if (!al16(x) || !al16(send_buf) || !al16(workspace) || !al4(topk_ids)) return MOE_ERR_INVALID;
   const size_t need = moe_dispatch_workspace_bytes(L.T, L.k, L.E);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_INVALID;
   char* ws = static_cast<char*>(workspace);
@@ -154,6 +166,9 @@ int expert_mlp(const void* send_buf, const float* a_scale, moe_dtype_t xdt, cons
   const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
   if (!w_gate_up || !w_down) return MOE_ERR_INVALID;
   if (rows > 0 && (!send_buf || !out_buf)) return MOE_ERR_INVALID;
+  if (!al16(send_buf) || !al16(w_gate_up) || !al16(w_down) || !al16(out_buf) || !al16(workspace) || !al16(y) ||
+      !al4(topk_w) || !al4(a_scale))
+    return MOE_ERR_INVALID;
   const size_t need = y ? moe_expert_mlp_combine_workspace_bytes(L.T, L.k, L.E, L.R, L.C, L.H, F, xdt)
                         : moe_expert_mlp_workspace_bytes(L.T, L.k, L.E, L.R, L.C, F, xdt);
   if (!workspace || workspace_bytes < need) return MOE_ERR_INVALID;
@@ -205,6 +220,7 @@ int moe_dispatch_fp8(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, co
   const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
   if (L.T > 0 && (!x || !topk_ids)) return MOE_ERR_INVALID;
   if (rows > 0 && (!send_q || !send_scale)) return MOE_ERR_INVALID;
+  if (!al16(x) || !al16(send_q) || !al16(workspace) || !al4(send_scale) || !al4(topk_ids)) return MOE_ERR_INVALID;
   const size_t need = moe_dispatch_workspace_bytes(L.T, L.k, L.E);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_INVALID;
   char* ws = static_cast<char*>(workspace);
@@ -238,6 +254,7 @@ int moe_combine(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* layout
   const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
   if (!topk_w || !y) return MOE_ERR_INVALID;
   if (rows > 0 && !out_buf) return MOE_ERR_INVALID;
+  if (!al16(out_buf) || !al16(y) || !al4(topk_w)) return MOE_ERR_INVALID;
   return hip_status(moe::launch_combine(out_buf, xdt == MOE_BF16, L, topk_w, y, stream));
 }
 
@@ -251,6 +268,7 @@ int moe_combine_send(const void* out_buf, moe_dtype_t xdt, const moe_layout_t* l
   const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
   if (!topk_w || !partial) return MOE_ERR_INVALID;
   if (rows > 0 && !out_buf) return MOE_ERR_INVALID;
+  if (!al16(out_buf) || !al16(partial) || !al4(topk_w)) return MOE_ERR_INVALID;
   return hip_status(moe::launch_combine_send(out_buf, xdt == MOE_BF16, L, topk_w, partial, stream));
 }
 
@@ -261,6 +279,7 @@ int moe_combine_recv(const void* partial, moe_dtype_t xdt, const moe_layout_t* l
   const moe_layout_t& L = *layout;
   if (L.T == 0) return MOE_OK;
   if (!partial || !y) return MOE_ERR_INVALID;
+  if (!al16(partial) || !al16(y)) return MOE_ERR_INVALID;
   return hip_status(moe::launch_combine_recv(partial, xdt == MOE_BF16, L, y, stream));
 }
 

@@ -23,6 +23,10 @@
  *     call only enqueues kernels on `stream` (NULL = the default stream) and returns.
  *   - Row-major layouts, 32-bit indices. Activations and expert weights share one type `xdt`
  *     (MOE_F32 or MOE_BF16); the router weight, bias, logits and routing weights are fp32.
+ *   - Alignment: activations, expert and router weights, send / output / partial rows (and fp8 codes)
+ *     and workspaces must be 16-byte aligned; int32 and fp32 arrays (ids, weights, logits, bias, block
+ *     scales, layout arrays) 4-byte aligned. Anything else is MOE_ERR_INVALID. hipMalloc and PyTorch
+ *     allocations are 256-byte aligned.
  *   - Return value: MOE_OK, or a negative status. Arguments are validated on the host before any
  *     HIP call; on MOE_ERR_INVALID / MOE_ERR_UNSUPPORTED nothing was enqueued. MOE_ERR_HIP means a
  *     launch failed (hipGetLastError); earlier kernels of the same call may have run.
@@ -45,7 +49,7 @@ typedef enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
 enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID = -1,     /* null pointer, out-of-range size, inconsistent layout */
+  MOE_ERR_INVALID = -1,     /* null or misaligned pointer, out-of-range size, inconsistent layout */
   MOE_ERR_UNSUPPORTED = -2, /* a shape or dtype the kernels do not handle (e.g. H % 8 != 0) */
   MOE_ERR_HIP = -3          /* a kernel launch failed */
 };

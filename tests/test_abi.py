@@ -158,6 +158,27 @@ def test_fused_combine_rejects_invalid_arguments_and_sizes_its_workspace(lib):
     assert call(_layout(R=3)) == MOE_ERR_INVALID
 
 
+def test_misaligned_pointers_are_rejected(lib):
+    ODD16 = ctypes.c_void_p(0x1008)   # 8-byte aligned, not 16
+    ODD4 = ctypes.c_void_p(0x1002)    # 2-byte aligned
+    L = _layout()
+    # activations and rows need 16 bytes, int / fp32 arrays 4
+    assert lib.moe_dispatch(ODD16, moe.MOE_BF16, FAKE, ctypes.byref(L), FAKE, FAKE, 1 << 30, None) == MOE_ERR_INVALID
+    assert lib.moe_dispatch(FAKE, moe.MOE_BF16, ODD4, ctypes.byref(L), FAKE, FAKE, 1 << 30, None) == MOE_ERR_INVALID
+    assert lib.moe_combine(FAKE, moe.MOE_BF16, ctypes.byref(L), FAKE, ODD16, None) == MOE_ERR_INVALID
+    assert lib.moe_combine(FAKE, moe.MOE_BF16, ctypes.byref(L), ODD4, FAKE, None) == MOE_ERR_INVALID
+    assert lib.moe_expert_mlp(FAKE, moe.MOE_BF16, ctypes.byref(L), ODD16, FAKE, 64, FAKE, FAKE, 1 << 30, None) == \
+        MOE_ERR_INVALID
+    assert lib.moe_route(ODD16, moe.MOE_BF16, FAKE, None, 0, 16, 64, 8, 2, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == \
+        MOE_ERR_INVALID
+    assert lib.moe_combine_recv(ODD16, moe.MOE_BF16, ctypes.byref(L), FAKE, None) == MOE_ERR_INVALID
+    # a misaligned layout array
+    arr = [FAKE.value] * 7
+    arr[6] = ODD4.value
+    bad = moe._CLayout(16, 2, 8, 1, 4, 64, *arr)
+    assert lib.moe_combine(FAKE, moe.MOE_BF16, ctypes.byref(bad), FAKE, FAKE, None) == MOE_ERR_INVALID
+
+
 def test_sender_side_combine_rejects_invalid_arguments(lib):
     L = _layout(R=2)
     assert lib.moe_combine_send(FAKE, moe.MOE_BF16, ctypes.byref(L), FAKE, None, None) == MOE_ERR_INVALID
