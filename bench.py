@@ -232,8 +232,9 @@ def main():
         return
     if args.calibrate_gemm:
         import torch
+        cfg = pick_workload(args.workload)
         torch.cuda.set_device(0)
-        calibrate_gemm(pick_workload(args.workload))
+        calibrate_gemm(cfg)
         return
 
     import torch
