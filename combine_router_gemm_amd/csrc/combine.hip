@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out_
   __shared__ float s_w[MOE_MAX_TOPK];
   const int t = blockIdx.x / chunks;
   const int v0 = (blockIdx.x % chunks) * 256 * VPT + threadIdx.x;
-  if (threadIdx.x < k) {
+  if ((int)threadIdx.x < k) {
     s_row[threadIdx.x] = pair_row[(int64_t)t * k + threadIdx.x];
     s_w[threadIdx.x] = topk_w[(int64_t)t * k + threadIdx.x];
   }
@@ -107,14 +107,14 @@ __global__ __launch_bounds__(256) void combine_send_kernel(const T* __restrict__
   __shared__ unsigned s_members[MOE_MAX_TOPK];
   const int t = blockIdx.x / chunks;
   const int v0 = (blockIdx.x % chunks) * 256 * VPT + threadIdx.x;
-  if (threadIdx.x < k) {
+  if ((int)threadIdx.x < k) {
     const int row = pair_row[(int64_t)t * k + threadIdx.x];
     s_row[threadIdx.x] = row;
     s_w[threadIdx.x] = topk_w[(int64_t)t * k + threadIdx.x];
     s_rank[threadIdx.x] = row >= 0 ? row_rank(row, offset, El, R) : -1;
   }
   __syncthreads();
-  if (threadIdx.x < k) {
+  if ((int)threadIdx.x < k) {
     const int j = threadIdx.x, r = s_rank[j];
     unsigned m = 0;
     bool lead = r >= 0;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void combine_recv_kernel(const T* __restrict__
   __shared__ int s_nr;
   const int t = blockIdx.x / chunks;
   const int v0 = (blockIdx.x % chunks) * 256 * VPT + threadIdx.x;
-  if (threadIdx.x < k) {
+  if ((int)threadIdx.x < k) {
     const int row = pair_row[(int64_t)t * k + threadIdx.x];
     s_rank[threadIdx.x] = row >= 0 ? row_rank(row, offset, El, R) : -1;
   }

@@ -57,17 +57,6 @@ __device__ __forceinline__ void load8_f32<float>(const float* base, int64_t ld, 
   }
 }
 
-template <>
-__device__ __forceinline__ void load8_f32<bf16_t>(const bf16_t* base, int64_t ld, int r, int nrows, int kc,
-                                                  int kend, float (&o)[8]) {
-  if (r < nrows && kc < kend) {
-    unpack(ld16(base + (int64_t)r * ld + kc), o);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = 0.f;
-  }
-}
-
 // grid: (ceil(T/64), ceil(E/64), splits); block 256 = 4 waves in 2x2, each wave a 32x32 output tile.
 template <typename TX>
 __global__ __launch_bounds__(256) void route_gemm_kernel(const TX* __restrict__ x, const float* __restrict__ w,
