@@ -28,7 +28,7 @@ METRIC = "MoE-layer tokens/s on 1 MI355X; dispatch+combine GB/s and % HBM peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_F32_PEAK_TFLOPS = 157.3
-DEFAULT_WORKLOAD = 2            # Mixtral-8x7B-shaped decode layer
+DEFAULT_WORKLOAD = "mixtral8x7b-decode"
 
 
 def parse():
@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=32)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=None,
-                    help="workload name or number (default: mixtral8x7b-decode)")
+                    help="workload name, or its position (1-5) in moe_workloads.WORKLOADS "
+                         "(default: mixtral8x7b-decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--fused-combine", action="store_true",
                     help="fuse the combine into the expert MLP's down GEMM (moe_expert_mlp_combine): the tile "
@@ -149,11 +150,13 @@ def calibrate_gemm(cfg, reps: int = 20) -> None:
 def pick_workload(name):
     import moe_workloads as W
     if name is None:
-        return W.CONFIGS[DEFAULT_WORKLOAD]
-    for c in W.CONFIGS.values():
-        if name == c.name or name == str(c.idx):
-            return c
-    raise SystemExit(f"unknown workload {name!r}; choose from {[c.name for c in W.CONFIGS.values()]}")
+        return W.workload(DEFAULT_WORKLOAD)
+    names = list(W.WORKLOADS)
+    if name in W.WORKLOADS:
+        return W.WORKLOADS[name]
+    if name.isdigit() and 1 <= int(name) <= len(names):   # position in the listing, from 1
+        return W.WORKLOADS[names[int(name) - 1]]
+    raise SystemExit(f"unknown workload {name!r}; choose from {names}")
 
 
 def algorithmic_bytes(cfg, C, counts, s, fp8=False, sender=False):

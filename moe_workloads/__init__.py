@@ -24,7 +24,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["MoEConfig", "CONFIGS", "capacity", "rows_max", "make_inputs", "make_routing_bias",
+__all__ = ["MoEConfig", "WORKLOADS", "workload", "capacity", "rows_max", "make_inputs", "make_routing_bias",
            "make_expert_weights", "seed_for"]
 
 
@@ -37,8 +37,9 @@ class MoEConfig:
     rational ``cf_num / cf_den``; ``cf_num == 0`` means "no capacity drop" (capacity = T).
     ``dtype`` is the activation / expert-weight type ("f32" or "bf16"); the router is always fp32.
     ``routing`` is the routing structure: "uniform", "balanced", "zipf" or "hot8".
+    ``seed`` selects the workload's random streams (see seed_for).
     """
-    idx: int
+    seed: int
     name: str
     T: int
     H: int
@@ -56,18 +57,27 @@ class MoEConfig:
         return self.E // self.R
 
 
-CONFIGS = {
-    1: MoEConfig(1, "tiny-fp32", T=256, H=128, E=8, k=2, F=256, R=1, cf_num=5, cf_den=4,
-                 dtype="f32", routing="uniform"),
-    2: MoEConfig(2, "mixtral8x7b-decode", T=128, H=4096, E=8, k=2, F=14336, R=1, cf_num=0, cf_den=1,
-                 dtype="bf16", routing="uniform"),
-    3: MoEConfig(3, "dsv3-prefill-ep8-share", T=4096, H=7168, E=256, k=8, F=2048, R=8, cf_num=1,
-                 cf_den=1, dtype="bf16", routing="balanced"),
-    4: MoEConfig(4, "kimik2-decode-ep8-share", T=128, H=7168, E=384, k=8, F=2048, R=8, cf_num=5,
-                 cf_den=4, dtype="bf16", routing="zipf"),
-    5: MoEConfig(5, "large-skewed-prefill", T=16384, H=7168, E=256, k=8, F=2048, R=1, cf_num=1,
-                 cf_den=1, dtype="bf16", routing="hot8"),
-}
+# the five workloads, by name (the order is the benchmark's listing order)
+WORKLOADS = {c.name: c for c in (
+    MoEConfig(1, "tiny-fp32", T=256, H=128, E=8, k=2, F=256, R=1, cf_num=5, cf_den=4,
+              dtype="f32", routing="uniform"),
+    MoEConfig(2, "mixtral8x7b-decode", T=128, H=4096, E=8, k=2, F=14336, R=1, cf_num=0, cf_den=1,
+              dtype="bf16", routing="uniform"),
+    MoEConfig(3, "dsv3-prefill-ep8-share", T=4096, H=7168, E=256, k=8, F=2048, R=8, cf_num=1,
+              cf_den=1, dtype="bf16", routing="balanced"),
+    MoEConfig(4, "kimik2-decode-ep8-share", T=128, H=7168, E=384, k=8, F=2048, R=8, cf_num=5,
+              cf_den=4, dtype="bf16", routing="zipf"),
+    MoEConfig(5, "large-skewed-prefill", T=16384, H=7168, E=256, k=8, F=2048, R=1, cf_num=1,
+              cf_den=1, dtype="bf16", routing="hot8"),
+)}
+
+
+def workload(name: str) -> MoEConfig:
+    """The workload called `name`."""
+    try:
+        return WORKLOADS[name]
+    except KeyError:
+        raise KeyError(f"unknown workload {name!r}; choose from {list(WORKLOADS)}") from None
 
 
 def capacity(cfg: MoEConfig, T: Optional[int] = None) -> int:
@@ -88,8 +98,8 @@ def rows_max(T: int, k: int, E: int, C: int) -> int:
     return min(T * k, E * C)
 
 
-def seed_for(cfg_idx: int, tensor_id: int, l: int = 0) -> int:
-    return (cfg_idx << 32) | (tensor_id << 16) | l
+def seed_for(seed: int, tensor_id: int, l: int = 0) -> int:
+    return (seed << 32) | (tensor_id << 16) | l
 
 
 def _gen(device, seed: int) -> torch.Generator:
@@ -119,7 +129,7 @@ def make_routing_bias(cfg: MoEConfig, device="cpu") -> tuple[Optional[torch.Tens
         e = torch.arange(E, dtype=torch.float64)
         return (-1.2 * torch.log(e + 1.0)).to(torch.float32).to(device), 0
     if cfg.routing == "balanced":
-        g = _gen("cpu", seed_for(cfg.idx, 4))
+        g = _gen("cpu", seed_for(cfg.seed, 4))
         pi_E = torch.randperm(E, generator=g)
         pi_T = torch.randperm(T, generator=g)
         cols = (pi_T.view(T, 1) * k + torch.arange(k).view(1, k)) % E
@@ -139,9 +149,9 @@ def make_expert_weights(cfg: MoEConfig, l: int, device="cpu") -> tuple[torch.Ten
     N(0, 0.02^2) drawn in fp32 then rounded to the activation type (round-to-nearest-even).
     """
     dt = _act_dtype(cfg)
-    gu = torch.randn(2 * cfg.F, cfg.H, generator=_gen(device, seed_for(cfg.idx, 2, l)),
+    gu = torch.randn(2 * cfg.F, cfg.H, generator=_gen(device, seed_for(cfg.seed, 2, l)),
                      device=device, dtype=torch.float32).mul_(0.02).to(dt)
-    dn = torch.randn(cfg.H, cfg.F, generator=_gen(device, seed_for(cfg.idx, 3, l)),
+    dn = torch.randn(cfg.H, cfg.F, generator=_gen(device, seed_for(cfg.seed, 3, l)),
                      device=device, dtype=torch.float32).mul_(0.02).to(dt)
     return gu, dn
 
@@ -157,9 +167,9 @@ def make_inputs(cfg: MoEConfig, device="cpu", T: Optional[int] = None,
     T_full = cfg.T
     T = T_full if T is None else T
     dt = _act_dtype(cfg)
-    x = torch.randn(T_full, cfg.H, generator=_gen(device, seed_for(cfg.idx, 0)), device=device,
+    x = torch.randn(T_full, cfg.H, generator=_gen(device, seed_for(cfg.seed, 0)), device=device,
                     dtype=torch.float32)[:T].to(dt).contiguous()
-    w_router = torch.randn(cfg.E, cfg.H, generator=_gen(device, seed_for(cfg.idx, 1)),
+    w_router = torch.randn(cfg.E, cfg.H, generator=_gen(device, seed_for(cfg.seed, 1)),
                            device=device, dtype=torch.float32).mul_(0.02)
     bias, stride = make_routing_bias(cfg, device)
     if bias is not None and stride != 0:
@@ -185,6 +195,6 @@ def small_config(base: MoEConfig, **overrides) -> MoEConfig:
 
 
 def describe(cfg: MoEConfig) -> str:
-    return (f"cfg{cfg.idx} {cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} F={cfg.F} "
+    return (f"{cfg.name}: T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} F={cfg.F} "
             f"R={cfg.R} C={capacity(cfg)} {cfg.dtype} {cfg.routing}")
 

@@ -17,3 +17,21 @@ def test_unknown_workload_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "no-such-layer"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0 and "unknown workload" in (r.stderr + r.stdout)
+
+
+def test_workload_by_name_or_position():
+    sys.path.insert(0, ROOT)
+    import bench
+    import moe_workloads as W
+    names = list(W.WORKLOADS)
+    assert bench.pick_workload(None).name == bench.DEFAULT_WORKLOAD == "mixtral8x7b-decode"
+    for i, n in enumerate(names):
+        assert bench.pick_workload(n) is W.WORKLOADS[n]
+        assert bench.pick_workload(str(i + 1)) is W.WORKLOADS[n]
+    for bad in ("0", str(len(names) + 1), "mixtral"):
+        try:
+            bench.pick_workload(bad)
+        except SystemExit as e:
+            assert "unknown workload" in str(e)
+        else:
+            raise AssertionError(bad)

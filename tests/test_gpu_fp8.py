@@ -26,20 +26,21 @@ pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
 FP8_VS_BF16 = 0.1
-CFGS = [2, 3, 4, 5]
-FULL = {2, 4}
+WORKLOADS = ["mixtral8x7b-decode", "dsv3-prefill-ep8-share", "kimik2-decode-ep8-share", "large-skewed-prefill"]
+# workloads the oracle finishes whole in seconds (the others are sampled)
+FULL = {"mixtral8x7b-decode", "kimik2-decode-ep8-share"}
 
 _cache = {}
 
 
-def _layer(cfg_idx):
-    if cfg_idx not in _cache:
-        cfg = W.CONFIGS[cfg_idx]
+def _layer(wl):
+    if wl not in _cache:
+        cfg = W.workload(wl)
         print(f"\n[gpu] fp8 path: {W.describe(cfg)}", flush=True)
         inp = W.make_inputs(cfg, device="cuda")
         _cache.clear()
-        _cache[cfg_idx] = (cfg, inp, run_layer_fp8(inp, cfg.k, cfg.R))
-    return _cache[cfg_idx]
+        _cache[wl] = (cfg, inp, run_layer_fp8(inp, cfg.k, cfg.R))
+    return _cache[wl]
 
 
 def _bias_np(inp):
@@ -67,27 +68,27 @@ def _check_dispatch(cfg, inp, out, rows=None):
     return lay
 
 
-@pytest.mark.parametrize("cfg_idx", CFGS)
-def test_f3_dispatch_fp8(cfg_idx):
-    cfg, inp, out = _layer(cfg_idx)
+@pytest.mark.parametrize("wl", WORKLOADS)
+def test_f3_dispatch_fp8(wl):
+    cfg, inp, out = _layer(wl)
     n = int(to_np(out["layout"].expert_offset)[cfg.E])
     rows = None
-    if cfg_idx not in FULL and n > 2048:
-        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(cfg_idx).choice(n, 2048, replace=False)]))
+    if wl not in FULL and n > 2048:
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(cfg.seed).choice(n, 2048, replace=False)]))
     _check_dispatch(cfg, inp, out, rows)
-    print(f"[gpu] cfg{cfg_idx}: fp8 rows checked {n if rows is None else len(rows)} of {n}")
+    print(f"[gpu] {wl}: fp8 rows checked {n if rows is None else len(rows)} of {n}")
 
 
-@pytest.mark.parametrize("cfg_idx", CFGS)
-def test_f4_expert_mlp_fp8(cfg_idx):
-    cfg, inp, out = _layer(cfg_idx)
+@pytest.mark.parametrize("wl", WORKLOADS)
+def test_f4_expert_mlp_fp8(wl):
+    cfg, inp, out = _layer(wl)
     offset = to_np(out["layout"].expert_offset)
     rex = oracle.row_experts(offset, cfg.E)
     total = int(offset[cfg.E])
-    if cfg_idx in FULL:
+    if wl in FULL:
         rows = np.arange(total)
     else:
-        rng = np.random.default_rng(100 + cfg_idx)
+        rng = np.random.default_rng(100 + cfg.seed)
         local = rex % cfg.El
         chosen = rng.choice(np.unique(local), size=min(6, len(np.unique(local))), replace=False)
         rows = []
@@ -104,7 +105,7 @@ def test_f4_expert_mlp_fp8(cfg_idx):
     got = to_np(out["out_buf"][idx])
     err = rowwise_rel_err(oracle.to_f64(got, "bf16"), oracle.to_f64(ref, "bf16"))
     assert np.all(err <= TOL), f"max rel err {err.max():.3e} over {len(rows)} rows"
-    print(f"[gpu] cfg{cfg_idx}: fp8 MLP rows checked {len(rows)}, max rel err {err.max():.2e}")
+    print(f"[gpu] {wl}: fp8 MLP rows checked {len(rows)}, max rel err {err.max():.2e}")
 
 
 def _oracle_layer_fp8(cfg, inp, ids, C, tokens):
@@ -127,11 +128,11 @@ def _oracle_layer_fp8(cfg, inp, ids, C, tokens):
     return oracle.combine(out_rows, "bf16", pr_local, w)
 
 
-@pytest.mark.parametrize("cfg_idx", CFGS)
-def test_f6_layer_fp8_and_distance_to_bf16(cfg_idx):
-    cfg, inp, out = _layer(cfg_idx)
+@pytest.mark.parametrize("wl", WORKLOADS)
+def test_f6_layer_fp8_and_distance_to_bf16(wl):
+    cfg, inp, out = _layer(wl)
     ids = to_np(out["ids"])
-    tokens = np.arange(cfg.T) if cfg_idx in FULL else np.sort(np.random.default_rng(21).choice(cfg.T, 48, replace=False))
+    tokens = np.arange(cfg.T) if wl in FULL else np.sort(np.random.default_rng(21).choice(cfg.T, 48, replace=False))
     ref = _oracle_layer_fp8(cfg, inp, ids, inp["C"], tokens)
     y = oracle.to_f64(to_np(out["y"])[tokens], "bf16")
     err = rowwise_rel_err(y, oracle.to_f64(ref, "bf16"))
@@ -145,7 +146,7 @@ def test_f6_layer_fp8_and_distance_to_bf16(cfg_idx):
     live = ~dropped
     dev = rowwise_rel_err(y[live], yb[live])
     assert np.all(dev <= FP8_VS_BF16), f"fp8 vs bf16 worst token {dev.max():.3f}"
-    print(f"[gpu] cfg{cfg_idx}: fp8 layer tokens {len(tokens)}, max rel err {err.max():.2e}; "
+    print(f"[gpu] {wl}: fp8 layer tokens {len(tokens)}, max rel err {err.max():.2e}; "
           f"distance to the bf16 layer mean {dev.mean():.3f}, max {dev.max():.3f}")
     del bf
 
@@ -170,8 +171,8 @@ EDGE = [
 
 @pytest.mark.parametrize("name,T,H,E,k,F,R,C,routing", EDGE, ids=[e[0] for e in EDGE])
 def test_fp8_edge_cases(name, T, H, E, k, F, R, C, routing):
-    cfg = W.small_config(W.CONFIGS[2], idx=400 + [e[0] for e in EDGE].index(name), name=name, T=max(T, 1), H=H,
-                         E=E, k=k, F=F, R=R, dtype="bf16", routing=routing)
+    cfg = W.small_config(W.workload("mixtral8x7b-decode"), seed=400 + [e[0] for e in EDGE].index(name), name=name,
+                         T=max(T, 1), H=H, E=E, k=k, F=F, R=R, dtype="bf16", routing=routing)
     inp = W.make_inputs(cfg, device="cuda", T=T)
     inp["C"] = C
     if name == "extreme_rows":

@@ -43,14 +43,14 @@ def _check_fused(inp, out, k, R, calls=3):
     return total
 
 
-@pytest.mark.parametrize("cfg_idx", [1, 2, 3, 4, 5])
-def test_fused_combine_full_size(cfg_idx):
-    cfg = W.CONFIGS[cfg_idx]
+@pytest.mark.parametrize("wl", list(W.WORKLOADS))
+def test_fused_combine_full_size(wl):
+    cfg = W.workload(wl)
     print(f"\n[gpu] fused combine: {W.describe(cfg)}", flush=True)
     inp = W.make_inputs(cfg, device="cuda")
     out = run_layer(inp, cfg.k, cfg.R)
     total = _check_fused(inp, out, cfg.k, cfg.R)
-    print(f"[gpu] cfg{cfg_idx}: fused combine equals moe_expert_mlp + moe_combine on {cfg.T} tokens, {total} rows")
+    print(f"[gpu] {wl}: fused combine equals moe_expert_mlp + moe_combine on {cfg.T} tokens, {total} rows")
     del out, inp
     torch.cuda.empty_cache()
 
@@ -76,8 +76,8 @@ EDGE = [
 
 @pytest.mark.parametrize("name,T,H,E,k,F,R,C,dtype,routing", EDGE, ids=[e[0] for e in EDGE])
 def test_fused_combine_edge_cases(name, T, H, E, k, F, R, C, dtype, routing):
-    cfg = W.small_config(W.CONFIGS[1], idx=600 + [e[0] for e in EDGE].index(name), name=name, T=max(T, 1), H=H,
-                         E=E, k=k, F=F, R=R, dtype=dtype, routing=routing)
+    cfg = W.small_config(W.workload("tiny-fp32"), seed=600 + [e[0] for e in EDGE].index(name), name=name,
+                         T=max(T, 1), H=H, E=E, k=k, F=F, R=R, dtype=dtype, routing=routing)
     inp = W.make_inputs(cfg, device="cuda", T=T)
     inp["C"] = C
     print(f"\n[gpu] fused combine edge case {name}", flush=True)

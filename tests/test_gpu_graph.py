@@ -27,8 +27,8 @@ def _bits(t):
 
 @pytest.mark.parametrize("name,T,H,E,k,F,R,C,routing", CASES, ids=[c[0] for c in CASES])
 def test_graph_replay_matches_eager(name, T, H, E, k, F, R, C, routing):
-    cfg = W.small_config(W.CONFIGS[2], idx=300 + [c[0] for c in CASES].index(name), name=name, T=T, H=H, E=E, k=k,
-                         F=F, R=R, dtype="bf16", routing=routing)
+    cfg = W.small_config(W.workload("mixtral8x7b-decode"), seed=300 + [c[0] for c in CASES].index(name), name=name,
+                         T=T, H=H, E=E, k=k, F=F, R=R, dtype="bf16", routing=routing)
     dev = torch.device("cuda:0")
     inp = W.make_inputs(cfg, device=dev, T=T)
     x = inp["x"]
@@ -91,8 +91,8 @@ VARIANT_CASES = [
 
 @pytest.mark.parametrize("name,T,H,E,k,F,R,C,routing", VARIANT_CASES, ids=[c[0] for c in VARIANT_CASES])
 def test_graph_replay_fp8_and_sender_side_combine(name, T, H, E, k, F, R, C, routing):
-    cfg = W.small_config(W.CONFIGS[2], idx=320 + [c[0] for c in VARIANT_CASES].index(name), name=name, T=T, H=H,
-                         E=E, k=k, F=F, R=R, dtype="bf16", routing=routing)
+    cfg = W.small_config(W.workload("mixtral8x7b-decode"), seed=320 + [c[0] for c in VARIANT_CASES].index(name),
+                         name=name, T=T, H=H, E=E, k=k, F=F, R=R, dtype="bf16", routing=routing)
     dev = torch.device("cuda:0")
     inp = W.make_inputs(cfg, device=dev, T=T)
     x = inp["x"]

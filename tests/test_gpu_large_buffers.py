@@ -19,8 +19,8 @@ pytestmark = pytest.mark.gpu
 
 def test_send_and_output_buffers_above_2_gib():
     T, H, E, k, F, R, C = 16384, 8704, 64, 8, 256, 1, 4096
-    cfg = W.small_config(W.CONFIGS[3], idx=800, name="large_buffers", T=T, H=H, E=E, k=k, F=F, R=R, dtype="bf16",
-                         routing="uniform")
+    cfg = W.small_config(W.workload("dsv3-prefill-ep8-share"), seed=800, name="large_buffers", T=T, H=H, E=E, k=k,
+                         F=F, R=R, dtype="bf16", routing="uniform")
     print(f"\n[gpu] large buffers: T={T} H={H} E={E} k={k} F={F} R={R} C={C} bf16 uniform", flush=True)
     inp = W.make_inputs(cfg, device="cuda")
     inp["C"] = C

@@ -27,33 +27,33 @@ TOL = {"bf16": 2e-2, "f32": 1e-4}
 _cache = {}
 
 
-def _layer(cfg_idx):
+def _layer(wl):
     """Inputs (device) and HIP outputs of one full-size workload, computed once per session."""
-    if cfg_idx not in _cache:
-        cfg = W.CONFIGS[cfg_idx]
+    if wl not in _cache:
+        cfg = W.workload(wl)
         print(f"\n[gpu] running {W.describe(cfg)}", flush=True)
         inp = W.make_inputs(cfg, device="cuda")
         out = run_layer(inp, cfg.k, cfg.R)
-        _cache[cfg_idx] = (cfg, inp, out)
-    return _cache[cfg_idx]
+        _cache[wl] = (cfg, inp, out)
+    return _cache[wl]
 
 
 def _bias_np(inp):
     return None if inp["bias"] is None else to_np(inp["bias"])
 
 
-CFGS = [1, 2, 3, 4, 5]
+WORKLOADS = list(W.WORKLOADS)
 # workloads whose whole expert MLP the oracle finishes in seconds (the others are sampled)
-FULL_MLP = {1, 2, 4}
+FULL_MLP = {"tiny-fp32", "mixtral8x7b-decode", "kimik2-decode-ep8-share"}
 
 
 def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else (t.view(torch.int32) if t.dtype == torch.float32 else t)
 
 
-@pytest.mark.parametrize("cfg_idx", CFGS)
-def test_p1_p2_route(cfg_idx):
-    cfg, inp, out = _layer(cfg_idx)
+@pytest.mark.parametrize("wl", WORKLOADS)
+def test_p1_p2_route(wl):
+    cfg, inp, out = _layer(wl)
     dt = dt_name(inp["x"])
     x = to_np(inp["x"])
     ref = oracle.router_logits(x, dt, to_np(inp["w_router"]), _bias_np(inp))
@@ -73,13 +73,13 @@ def test_p1_p2_route(cfg_idx):
         srt = np.sort(ref[t].astype(np.float64))[::-1]
         gap = srt[cfg.k - 1] - srt[cfg.k]
         assert gap <= 2e-5 * scale[t], (t, gap)
-    print(f"[gpu] cfg{cfg_idx}: logits worst row ratio {np.max(err / scale):.2e}, top-k flips vs oracle's "
+    print(f"[gpu] {wl}: logits worst row ratio {np.max(err / scale):.2e}, top-k flips vs oracle's "
           f"own logits {len(flips)}")
 
 
-@pytest.mark.parametrize("cfg_idx", CFGS)
-def test_p3_dispatch(cfg_idx):
-    cfg, inp, out = _layer(cfg_idx)
+@pytest.mark.parametrize("wl", WORKLOADS)
+def test_p3_dispatch(wl):
+    cfg, inp, out = _layer(wl)
     dt = dt_name(inp["x"])
     lay, sb = oracle.dispatch(to_np(inp["x"]), dt, to_np(out["ids"]), cfg.E, inp["C"], cfg.R)
     L = out["layout"]
@@ -92,7 +92,7 @@ def test_p3_dispatch(cfg_idx):
     # the invariants the pages state: counts = router histogram, overflow = max(count - C, 0)
     ids = to_np(out["ids"])
     assert np.array_equal(lay.expert_count, np.bincount(ids.ravel(), minlength=cfg.E))
-    print(f"[gpu] cfg{cfg_idx}: rows {n} of {cfg.T * cfg.k} pairs, overflow {int(lay.expert_overflow.sum())}, "
+    print(f"[gpu] {wl}: rows {n} of {cfg.T * cfg.k} pairs, overflow {int(lay.expert_overflow.sum())}, "
           f"experts over capacity {int((lay.expert_overflow > 0).sum())}")
 
 
@@ -115,15 +115,15 @@ def _sample_rows(offset_l, BM=128, per_expert=10, max_experts=6, seed=0):
     return out
 
 
-@pytest.mark.parametrize("cfg_idx", CFGS)
-def test_p4_expert_mlp(cfg_idx):
-    cfg, inp, out = _layer(cfg_idx)
+@pytest.mark.parametrize("wl", WORKLOADS)
+def test_p4_expert_mlp(wl):
+    cfg, inp, out = _layer(wl)
     dt = dt_name(inp["x"])
     L = out["layout"]
     offset = to_np(L.expert_offset)
     rex = oracle.row_experts(offset, cfg.E)
     total = int(offset[cfg.E])
-    if cfg_idx in FULL_MLP:
+    if wl in FULL_MLP:
         rows = np.arange(total)
     else:
         # plan order groups rows by local expert; sample per local expert over all rank segments
@@ -132,7 +132,7 @@ def test_p4_expert_mlp(cfg_idx):
         rows = []
         per_l = [np.nonzero(local == l)[0] for l in range(El)]
         off_l = np.concatenate([[0], np.cumsum([len(p) for p in per_l])])
-        for l, picks in _sample_rows(off_l, seed=cfg_idx).items():
+        for l, picks in _sample_rows(off_l, seed=cfg.seed).items():
             rows += [int(per_l[l][p - off_l[l]]) for p in picks]
         rows = np.array(sorted(set(rows)), dtype=np.int64)
     sb = to_np(out["send_buf"][torch.as_tensor(rows, device="cuda")]) if len(rows) else None
@@ -144,12 +144,12 @@ def test_p4_expert_mlp(cfg_idx):
     f = oracle.to_f64
     err = rowwise_rel_err(f(got, dt), f(ref, dt))
     assert np.all(err <= TOL[dt]), f"max rel err {err.max():.3e} over {len(rows)} rows"
-    print(f"[gpu] cfg{cfg_idx}: MLP rows checked {len(rows)}, max rel err {err.max():.2e}")
+    print(f"[gpu] {wl}: MLP rows checked {len(rows)}, max rel err {err.max():.2e}")
 
 
-@pytest.mark.parametrize("cfg_idx", CFGS)
-def test_p5_combine(cfg_idx):
-    cfg, inp, out = _layer(cfg_idx)
+@pytest.mark.parametrize("wl", WORKLOADS)
+def test_p5_combine(wl):
+    cfg, inp, out = _layer(wl)
     dt = dt_name(inp["x"])
     L = out["layout"]
     pr = to_np(L.pair_row)
@@ -170,7 +170,7 @@ def test_p5_combine(cfg_idx):
     assert np.all(err <= TOL[dt]), f"max rel err {err.max():.3e}"
     dropped = (sub_pr < 0).all(axis=1)
     assert np.all(f(got, dt)[dropped] == 0.0)
-    print(f"[gpu] cfg{cfg_idx}: combine tokens {len(tokens)}, fully dropped {int(dropped.sum())}, "
+    print(f"[gpu] {wl}: combine tokens {len(tokens)}, fully dropped {int(dropped.sum())}, "
           f"max rel err {err.max():.2e}")
 
 
@@ -197,12 +197,12 @@ def _oracle_layer_tokens(cfg, inp, ids, C, tokens):
     return oracle.combine(out_rows, dt, pr_local, w)
 
 
-@pytest.mark.parametrize("cfg_idx", CFGS)
-def test_p6_layer_end_to_end(cfg_idx):
-    cfg, inp, out = _layer(cfg_idx)
+@pytest.mark.parametrize("wl", WORKLOADS)
+def test_p6_layer_end_to_end(wl):
+    cfg, inp, out = _layer(wl)
     dt = dt_name(inp["x"])
     ids = to_np(out["ids"])
-    if cfg_idx in FULL_MLP:
+    if wl in FULL_MLP:
         tokens = np.arange(cfg.T)
     else:
         tokens = np.sort(np.random.default_rng(11).choice(cfg.T, 48, replace=False))
@@ -211,11 +211,11 @@ def test_p6_layer_end_to_end(cfg_idx):
     f = oracle.to_f64
     err = rowwise_rel_err(f(got, dt), f(ref, dt))
     assert np.all(err <= TOL[dt]), f"max rel err {err.max():.3e}"
-    print(f"[gpu] cfg{cfg_idx}: layer tokens {len(tokens)}, max rel err {err.max():.2e}")
+    print(f"[gpu] {wl}: layer tokens {len(tokens)}, max rel err {err.max():.2e}")
 
 
 def test_determinism_bitwise():
-    cfg, inp, out = _layer(3)
+    cfg, inp, out = _layer("dsv3-prefill-ep8-share")
     again = run_layer(inp, cfg.k, cfg.R)
     for key in ("logits", "ids", "w", "send_buf", "out_buf", "y"):
         assert torch.equal(_bits(out[key]), _bits(again[key])), key
@@ -258,8 +258,8 @@ EDGE = [
 
 @pytest.mark.parametrize("name,T,H,E,k,F,R,C,dtype,routing", EDGE, ids=[e[0] for e in EDGE])
 def test_edge_cases(name, T, H, E, k, F, R, C, dtype, routing):
-    base = W.CONFIGS[1]
-    cfg = W.small_config(base, idx=100 + EDGE.index(next(e for e in EDGE if e[0] == name)), name=name,
+    base = W.workload("tiny-fp32")
+    cfg = W.small_config(base, seed=100 + EDGE.index(next(e for e in EDGE if e[0] == name)), name=name,
                          T=max(T, 1), H=H, E=E, k=k, F=F, R=R, dtype=dtype, routing=routing)
     inp = W.make_inputs(cfg, device="cuda", T=T)
     inp["C"] = C

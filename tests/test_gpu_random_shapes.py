@@ -74,7 +74,7 @@ def _id(i, kind, s):
                          ids=[_id(i, kd, s) for i, (kd, s) in enumerate(SHAPES)])
 def test_random_shape(i, kind, s):
     T, H, E, k, F, R, C = s["T"], s["H"], s["E"], s["k"], s["F"], s["R"], s["C"]
-    cfg = W.small_config(W.CONFIGS[1], idx=700 + i, name=f"random{i}", T=T, H=H, E=E, k=k, F=F, R=R,
+    cfg = W.small_config(W.workload("tiny-fp32"), seed=700 + i, name=f"random{i}", T=T, H=H, E=E, k=k, F=F, R=R,
                          dtype=s["dtype"], routing=s["routing"])
     print(f"\n[gpu] random shape {_id(i, kind, s)}", flush=True)
     inp = W.make_inputs(cfg, device="cuda", T=T)

@@ -93,16 +93,16 @@ def _check(cfg_E, R, out, partial, y, tokens):
     return int(present.sum()), int((pr >= 0).sum()), float(dev.max(initial=0.0))
 
 
-@pytest.mark.parametrize("cfg_idx", [1, 2, 3, 4, 5])
-def test_sender_side_combine_full_size(cfg_idx):
-    cfg = W.CONFIGS[cfg_idx]
+@pytest.mark.parametrize("wl", list(W.WORKLOADS))
+def test_sender_side_combine_full_size(wl):
+    cfg = W.workload(wl)
     print(f"\n[gpu] sender-side combine: {W.describe(cfg)}", flush=True)
     inp = W.make_inputs(cfg, device="cuda")
     out = run_layer(inp, cfg.k, cfg.R)
     partial, y = _run_send_recv(out, out["layout"], inp["x"].dtype)
     tokens = np.arange(cfg.T) if cfg.T <= 4096 else np.sort(np.random.default_rng(3).choice(cfg.T, 512, replace=False))
     p_rows, k_rows, dev = _check(cfg.E, cfg.R, out, partial, y, tokens)
-    print(f"[gpu] cfg{cfg_idx}: partial rows {p_rows} vs kept rows {k_rows} ({p_rows / max(k_rows, 1):.3f}); "
+    print(f"[gpu] {wl}: partial rows {p_rows} vs kept rows {k_rows} ({p_rows / max(k_rows, 1):.3f}); "
           f"max per-token distance to moe_combine {dev:.2e}")
     del out, partial, y, inp
     torch.cuda.empty_cache()
@@ -124,8 +124,8 @@ EDGE = [
 
 @pytest.mark.parametrize("name,T,H,E,k,F,R,C,dtype,routing", EDGE, ids=[e[0] for e in EDGE])
 def test_sender_side_combine_edge_cases(name, T, H, E, k, F, R, C, dtype, routing):
-    cfg = W.small_config(W.CONFIGS[1], idx=500 + [e[0] for e in EDGE].index(name), name=name, T=max(T, 1), H=H,
-                         E=E, k=k, F=F, R=R, dtype=dtype, routing=routing)
+    cfg = W.small_config(W.workload("tiny-fp32"), seed=500 + [e[0] for e in EDGE].index(name), name=name,
+                         T=max(T, 1), H=H, E=E, k=k, F=F, R=R, dtype=dtype, routing=routing)
     inp = W.make_inputs(cfg, device="cuda", T=T)
     inp["C"] = C
     print(f"\n[gpu] sender-side combine edge case {name}", flush=True)
