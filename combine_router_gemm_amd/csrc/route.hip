@@ -266,11 +266,13 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
   return (v > bv) || (v == bv && e < be);
 }
 
-// k rounds of a butterfly arg-max over G lanes (lane g holds the values of experts i * G + g; taken
-// marks values out of the running), then the softmax over the k winners; lanes g < k write slot g.
-template <int G, int VMAX>
+// k rounds of a butterfly arg-max over G lanes (lane g holds the values of experts i * G + g, or with
+// CONTIG of experts g * V + i; taken marks values out of the running), then the softmax over the k
+// winners; lanes g < k write slot g.
+template <int G, int VMAX, bool CONTIG = false>
 __device__ __forceinline__ void select_topk(const float (&val)[VMAX], bool (&taken)[VMAX], int g, int t, bool live,
-                                            int k, int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+                                            int k, int* __restrict__ topk_ids, float* __restrict__ topk_w,
+                                            int V = 1) {
   float sel_v[MOE_MAX_TOPK];
   int sel_e[MOE_MAX_TOPK];
 #pragma unroll
@@ -280,7 +282,7 @@ __device__ __forceinline__ void select_topk(const float (&val)[VMAX], bool (&tak
       int be = 0x7fffffff;
 #pragma unroll
       for (int i = 0; i < VMAX; ++i) {
-        const int e = i * G + g;
+        const int e = CONTIG ? g * V + i : i * G + g;
         if (!taken[i] && better(val[i], e, bv, be)) {
           bv = val[i];
           be = e;
@@ -297,8 +299,8 @@ __device__ __forceinline__ void select_topk(const float (&val)[VMAX], bool (&tak
       }
       sel_v[j] = bv;
       sel_e[j] = be;
-      if ((be & (G - 1)) == g) {
-        const int ii = be / G;
+      if ((CONTIG ? be / V : (be & (G - 1))) == g) {
+        const int ii = CONTIG ? be - g * V : be / G;
 #pragma unroll
         for (int i = 0; i < VMAX; ++i)
           if (i == ii) taken[i] = true;
@@ -380,6 +382,98 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, i
   }
 
   select_topk<G, VMAX>(val, taken, g, t, live, k, topk_ids, topk_w);
+}
+
+// E = 64 V (V <= 8): one wave per token, lane g holding the V consecutive experts g V .. g V + V - 1, so
+// the lane reads its part of each split's row with V / VW loads of VW floats (VW = 4, 2 or 1, dividing V,
+// with partial and logits aligned to it) instead of V single-float loads; the bias of the token is read
+// with its first split. Same sums, in the same order, as route_topk_kernel.
+template <int VW>
+__global__ __launch_bounds__(256) void route_topk_rows_kernel(const float* partial, int splits,
+                                                              const float* __restrict__ bias, int64_t bias_stride,
+                                                              int T, int E, int k, float* logits,
+                                                              int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  constexpr int VMAX = MOE_MAX_EXPERTS / 64;
+  const int g = threadIdx.x & 63;
+  const int t = (int)(((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6);
+  const bool live = t < T;  // the same for the whole wave
+  const int V = E >> 6;
+  const int64_t row = (int64_t)(live ? t : 0) * E + (int64_t)g * V;  // this lane's first value
+  auto load_row = [&](const float* p, float (&v)[VMAX]) {
+#pragma unroll
+    for (int i = 0; i < VMAX; i += VW) {
+      if (i < V) {
+        if (VW == 4) {
+          unpack(ld16(p + i), *reinterpret_cast<float(*)[4]>(&v[i]));
+        } else if (VW == 2) {
+          const f32x2 q = *reinterpret_cast<const f32x2*>(p + i);
+          v[i] = q.x;
+          v[i + 1] = q.y;
+        } else {
+          v[i] = p[i];
+        }
+      }
+    }
+  };
+  float sum[VMAX], b[VMAX];
+  bool taken[VMAX];
+#pragma unroll
+  for (int i = 0; i < VMAX; ++i) {
+    taken[i] = !(i < V && live);
+    sum[i] = 0.f;
+    b[i] = 0.f;
+  }
+  if (live) {
+    load_row(partial + row, sum);
+    if (bias) {
+      const float* pb = bias + (int64_t)t * bias_stride + (int64_t)g * V;
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i)
+        if (i < V) b[i] = pb[i];
+    }
+    // the remaining K-split partials, SPF splits in flight at a time, added in split order
+    constexpr int SPF = 4;
+    const int64_t TE = (int64_t)T * E;
+    for (int sp0 = 1; sp0 < splits; sp0 += SPF) {
+      float tmp[SPF][VMAX];
+#pragma unroll
+      for (int u = 0; u < SPF; ++u)
+        if (sp0 + u < splits) load_row(partial + (sp0 + u) * TE + row, tmp[u]);
+#pragma unroll
+      for (int u = 0; u < SPF; ++u)
+#pragma unroll
+        for (int i = 0; i < VMAX; ++i)
+          if (sp0 + u < splits && i < V) sum[i] += tmp[u][i];
+    }
+  }
+  float val[VMAX];
+#pragma unroll
+  for (int i = 0; i < VMAX; ++i) {
+    val[i] = -INFINITY;
+    if (!taken[i]) {
+      float s = sum[i];
+      if (bias) s += b[i];
+      sum[i] = s;
+      s = s + 0.0f;                       // -0 -> +0: equal values compare equal either way
+      val[i] = (s == s) ? s : -INFINITY;  // NaN ranks as -inf
+    }
+  }
+  if (live) {
+    float* pl = logits + row;
+#pragma unroll
+    for (int i = 0; i < VMAX; i += VW) {
+      if (i < V) {
+        if (VW == 4) {
+          st16(pl + i, pack(*reinterpret_cast<const float(*)[4]>(&sum[i])));
+        } else if (VW == 2) {
+          *reinterpret_cast<f32x2*>(pl + i) = f32x2{sum[i], sum[i + 1]};
+        } else {
+          pl[i] = sum[i];
+        }
+      }
+    }
+  }
+  select_topk<64, VMAX, true>(val, taken, g, t, live, k, topk_ids, topk_w, V);
 }
 
 // Few experts: one workgroup of 256 threads per token computes the logits directly. Thread i
@@ -512,6 +606,21 @@ hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, cons
   else
     route_gemm_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), w_router, T, H, E, k_split,
                                                        partial);
+  if (E % 64 == 0) {
+    const int V = E / 64;
+    const uintptr_t al = reinterpret_cast<uintptr_t>(partial) | reinterpret_cast<uintptr_t>(logits);
+    const int blocks = ceil_div_host(T, 4);  // four tokens (waves) per workgroup
+    if (V % 4 == 0 && al % 16 == 0)
+      route_topk_rows_kernel<4><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
+                                                            ids, wts);
+    else if (V % 2 == 0 && al % 8 == 0)
+      route_topk_rows_kernel<2><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
+                                                            ids, wts);
+    else
+      route_topk_rows_kernel<1><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
+                                                            ids, wts);
+    return hipGetLastError();
+  }
   // lane-group size: smallest power of two >= E, between 8 and 64
   int G = 8;
   while (G < E && G < 64) G *= 2;
