@@ -27,6 +27,9 @@ namespace {
 #ifndef ROUTE_FUSED_MAX_T
 #define ROUTE_FUSED_MAX_T 4096
 #endif
+#ifndef ROUTE_TOPK_WIDE_MAX_T
+#define ROUTE_TOPK_WIDE_MAX_T 1024
+#endif
 
 constexpr int RG_BM = 64;   // tokens per tile
 constexpr int RG_BN = 64;   // experts per tile
@@ -387,8 +390,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, i
 // E = 64 V (V <= 8): one wave per token, lane g holding the V consecutive experts g V .. g V + V - 1, so
 // the lane reads its part of each split's row with V / VW loads of VW floats (VW = 4, 2 or 1, dividing V,
 // with partial and logits aligned to it) instead of V single-float loads; the bias of the token is read
-// with its first split. Same sums, in the same order, as route_topk_kernel.
-template <int VW>
+// with its first split, and SPF further splits are in flight at a time. Same sums, in the same order, as
+// route_topk_kernel.
+template <int VW, int SPF>
 __global__ __launch_bounds__(256) void route_topk_rows_kernel(const float* partial, int splits,
                                                               const float* __restrict__ bias, int64_t bias_stride,
                                                               int T, int E, int k, float* logits,
@@ -431,8 +435,7 @@ __global__ __launch_bounds__(256) void route_topk_rows_kernel(const float* parti
       for (int i = 0; i < VMAX; ++i)
         if (i < V) b[i] = pb[i];
     }
-    // the remaining K-split partials, SPF splits in flight at a time, added in split order
-    constexpr int SPF = 4;
+    // the remaining K-split partials, added in split order
     const int64_t TE = (int64_t)T * E;
     for (int sp0 = 1; sp0 < splits; sp0 += SPF) {
       float tmp[SPF][VMAX];
@@ -610,15 +613,21 @@ hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, cons
     const int V = E / 64;
     const uintptr_t al = reinterpret_cast<uintptr_t>(partial) | reinterpret_cast<uintptr_t>(logits);
     const int blocks = ceil_div_host(T, 4);  // four tokens (waves) per workgroup
-    if (V % 4 == 0 && al % 16 == 0)
-      route_topk_rows_kernel<4><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
-                                                            ids, wts);
-    else if (V % 2 == 0 && al % 8 == 0)
-      route_topk_rows_kernel<2><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
-                                                            ids, wts);
-    else
-      route_topk_rows_kernel<1><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k, logits,
-                                                            ids, wts);
+    // with few tokens every split is loaded at once (latency); with many, four at a time (occupancy)
+    const bool wide = T <= ROUTE_TOPK_WIDE_MAX_T;
+#define MOE_ROUTE_ROWS(VW)                                                                                       \
+  do {                                                                                                         \
+    if (wide)                                                                                                  \
+      route_topk_rows_kernel<VW, ROUTE_MAX_SPLITS><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, \
+                                                                               T, E, k, logits, ids, wts);      \
+    else                                                                                                       \
+      route_topk_rows_kernel<VW, 4><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k,    \
+                                                                logits, ids, wts);                              \
+  } while (0)
+    if (V % 4 == 0 && al % 16 == 0) MOE_ROUTE_ROWS(4);
+    else if (V % 2 == 0 && al % 8 == 0) MOE_ROUTE_ROWS(2);
+    else MOE_ROUTE_ROWS(1);
+#undef MOE_ROUTE_ROWS
     return hipGetLastError();
   }
   // lane-group size: smallest power of two >= E, between 8 and 64
