@@ -81,17 +81,20 @@ __global__ __launch_bounds__(DR_THREADS) void dispatch_rank_kernel(const int* __
 
   int myrank[MOE_MAX_TOPK];
   int mye[MOE_MAX_TOPK];
+  // the ids of all k chunks in flight together, before the first ballot waits on one
+  int ide[MOE_MAX_TOPK];
+#pragma unroll
+  for (int c = 0; c < MOE_MAX_TOPK; ++c) {
+    const int64_t p = w_begin + (int64_t)c * 64 + lane;
+    ide[c] = (c < k && p < p_end) ? ids[p] : -1;
+  }
 #pragma unroll
   for (int c = 0; c < MOE_MAX_TOPK; ++c) {
     myrank[c] = 0;
     mye[c] = -1;
     if (c < k) {
-      const int64_t p = w_begin + (int64_t)c * 64 + lane;
-      int e = -1;
-      if (p < p_end) {
-        e = ids[p];
-        if (e < 0 || e >= E) e = -1;  // out-of-range ids are ignored
-      }
+      int e = ide[c];
+      if (e < 0 || e >= E) e = -1;  // out-of-range ids are ignored
       const bool valid = e >= 0;
       uint64_t same = __ballot(valid);
       for (int b = 0; b < nbits; ++b) {
