@@ -6,8 +6,8 @@
   cases with H = 128 also run the fp8 dispatch (codes and scales bit-exact).
 * top-k with exact ties: one-hot router rows make every logit exactly a chosen input value (from a small set
   including -0 and +0, optionally plus a per-expert bias), so most rows hold ties; the ids must equal the
-  oracle's top-k of the GPU logits (descending, ties to the lower id, -0 == +0) on both router kernels (the
-  fused small-E kernel and the split-K GEMM with the top-k kernel).
+  oracle's top-k of the GPU logits (descending, ties to the lower id, -0 == +0) on every router kernel (the
+  fused small-E kernel, and the split-K GEMM with the lane-interleaved or the row-contiguous top-k kernel).
 """
 import numpy as np
 import pytest
@@ -94,11 +94,31 @@ TOPK_CASES = [
 ]
 
 
+# E a multiple of 64 takes the row-contiguous top-k kernel: 2 to 8 values per lane (float4, float2 and single
+# loads), one split (the partial sums are the logits buffer) or several (extra zero-weight columns of x), few
+# tokens (all splits loaded at once) or many (four at a time), and a logits buffer only 4-byte aligned
+TOPK_ROWS_CASES = [
+    # T, E, k, bias, H, logits offset (floats)
+    (300, 128, 8, None, 128, 0), (1100, 192, 6, "vec", 2048, 0), (200, 320, 8, "rows", 4096, 0),
+    (700, 384, 8, None, 7168, 0), (50, 448, 7, "vec", 448, 1), (129, 512, 8, "rows", 1024, 1),
+    (1500, 256, 8, "rows", 256, 1), (3, 384, 8, None, 384, 0),
+]
+
+
 @pytest.mark.parametrize("T,E,k,bias", TOPK_CASES, ids=[f"T{c[0]}_E{c[1]}_k{c[2]}_{c[3]}" for c in TOPK_CASES])
 def test_topk_exact_ties(T, E, k, bias):
+    _check_topk_ties(T, E, k, bias, ((E + 7) // 8) * 8, 0)
+
+
+@pytest.mark.parametrize("T,E,k,bias,H,off", TOPK_ROWS_CASES,
+                         ids=[f"T{c[0]}_E{c[1]}_k{c[2]}_{c[3]}_H{c[4]}_off{c[5]}" for c in TOPK_ROWS_CASES])
+def test_topk_exact_ties_row_kernel(T, E, k, bias, H, off):
+    _check_topk_ties(T, E, k, bias, H, off)
+
+
+def _check_topk_ties(T, E, k, bias, H, off):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(T * 1000 + E)
-    H = ((E + 7) // 8) * 8
     vals = np.array([-2.0, -1.0, -0.0, 0.0, 0.5, 1.0, 2.0], dtype=np.float32)
     xv = rng.choice(vals, size=(T, H)).astype(np.float32)
     x = torch.as_tensor(xv).to(torch.bfloat16).to(dev)        # every value is exact in bf16
@@ -110,7 +130,7 @@ def test_topk_exact_ties(T, E, k, bias):
         b = torch.as_tensor(rng.choice([0.0, 1.0, -1.0], size=E).astype(np.float32), device=dev)
     elif bias == "rows":
         b = torch.as_tensor(rng.choice([0.0, 0.5], size=(T, E)).astype(np.float32), device=dev)
-    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    logits = torch.empty(T * E + off, dtype=torch.float32, device=dev)[off:].view(T, E)
     ids = torch.empty(T, k, dtype=torch.int32, device=dev)
     wts = torch.empty(T, k, dtype=torch.float32, device=dev)
     moe.moe_route(x, w, b, k, logits, ids, wts)
