@@ -9,8 +9,10 @@ runs at a size the oracle finishes in seconds:
   * the fused combine, bit for bit against moe_expert_mlp + moe_combine;
   * the sender-side combine against the oracle;
   * for bf16 shapes with H % 128 == 0, the fp8 dispatch (codes and scales bit-exact) and the fp8 layer.
+The environment variable MOE_RANDOM_SHAPES raises the number of shapes.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -58,8 +60,13 @@ def _draw(rng, kind):
 
 
 def _shapes():
+    """The 24 default shapes; MOE_RANDOM_SHAPES=N (N > 24) draws N - 24 more from the same stream, cycling
+    through the regimes (a longer run: `MOE_RANDOM_SHAPES=600 pytest tests/test_gpu_random_shapes.py`)."""
     rng = np.random.default_rng(20261203)
     kinds = ["dl"] * 4 + ["dec64"] * 4 + ["dec32"] * 4 + ["f32"] * 3 + ["regpre"] * 2 + ["any"] * 7
+    more = ["dl", "dec64", "dec32", "f32", "regpre", "any", "any", "any"]
+    n = max(len(kinds), int(os.environ.get("MOE_RANDOM_SHAPES", len(kinds))))
+    kinds += [more[i % len(more)] for i in range(n - len(kinds))]
     return [(kind, _draw(rng, kind)) for kind in kinds]
 
 
