@@ -269,13 +269,11 @@ __device__ __forceinline__ bool better(float v, int e, float bv, int be) {
   return (v > bv) || (v == bv && e < be);
 }
 
-// k rounds of a butterfly arg-max over G lanes (lane g holds the values of experts i * G + g, or with
-// CONTIG of experts g * V + i; taken marks values out of the running), then the softmax over the k
-// winners; lanes g < k write slot g.
-template <int G, int VMAX, bool CONTIG = false>
+// k rounds of a butterfly arg-max over G lanes (lane g holds the values of experts i * G + g; taken
+// marks values out of the running), then the softmax over the k winners; lanes g < k write slot g.
+template <int G, int VMAX>
 __device__ __forceinline__ void select_topk(const float (&val)[VMAX], bool (&taken)[VMAX], int g, int t, bool live,
-                                            int k, int* __restrict__ topk_ids, float* __restrict__ topk_w,
-                                            int V = 1) {
+                                            int k, int* __restrict__ topk_ids, float* __restrict__ topk_w) {
   float sel_v[MOE_MAX_TOPK];
   int sel_e[MOE_MAX_TOPK];
 #pragma unroll
@@ -285,7 +283,7 @@ __device__ __forceinline__ void select_topk(const float (&val)[VMAX], bool (&tak
       int be = 0x7fffffff;
 #pragma unroll
       for (int i = 0; i < VMAX; ++i) {
-        const int e = CONTIG ? g * V + i : i * G + g;
+        const int e = i * G + g;
         if (!taken[i] && better(val[i], e, bv, be)) {
           bv = val[i];
           be = e;
@@ -302,8 +300,8 @@ __device__ __forceinline__ void select_topk(const float (&val)[VMAX], bool (&tak
       }
       sel_v[j] = bv;
       sel_e[j] = be;
-      if ((CONTIG ? be / V : (be & (G - 1))) == g) {
-        const int ii = CONTIG ? be - g * V : be / G;
+      if ((be & (G - 1)) == g) {
+        const int ii = be / G;
 #pragma unroll
         for (int i = 0; i < VMAX; ++i)
           if (i == ii) taken[i] = true;
@@ -311,6 +309,81 @@ __device__ __forceinline__ void select_topk(const float (&val)[VMAX], bool (&tak
     }
   }
 
+  if (live && g < k) {
+    // softmax over the k selected logits (slot 0 holds the largest)
+    const float m = sel_v[0];
+    float sum = 0.f, mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        const float z = expf(sel_v[j] - m);
+        sum += z;
+        if (j == g) mine = z;
+      }
+    }
+    int myid = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j == g) myid = sel_e[j];
+    topk_ids[(int64_t)t * k + g] = myid;
+    topk_w[(int64_t)t * k + g] = mine / sum;
+  }
+}
+
+// Maximum of x over the 64 lanes of the wave, in every lane: DPP swaps within quads, 8- and 16-lane
+// mirrors (VALU operations, no LDS), then the four row maxima read into scalar registers.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// The selection of select_topk for one token per wave with lane g holding experts g * V + i (i < V): each
+// round takes every lane's best untaken value (the lowest i on ties), the wave maximum of those, and as
+// winner the lowest lane holding that maximum -- lanes hold ascending expert ranges, so that is the
+// lowest expert id among the equal values, the same (value desc, id asc) order. No LDS traffic: a DPP
+// maximum, a ballot and lane reads into scalar registers per round.
+template <int VMAX>
+__device__ __forceinline__ void select_topk_wave(const float (&val)[VMAX], bool (&taken)[VMAX], int g, int t,
+                                                 bool live, int k, int V, int* __restrict__ topk_ids,
+                                                 float* __restrict__ topk_w) {
+  float sel_v[MOE_MAX_TOPK];
+  int sel_e[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j < k) {
+      float bv = -INFINITY;
+      int bi = -1;
+#pragma unroll
+      for (int i = 0; i < VMAX; ++i) {
+        if (!taken[i] && (bi < 0 || val[i] > bv)) {
+          bv = val[i];
+          bi = i;
+        }
+      }
+      const float m = wave_max(bv);
+      const uint64_t cand = __ballot(bi >= 0 && bv == m);
+      const int wl = __builtin_ctzll(cand);  // k <= E: some lane still holds a value
+      const int we = __builtin_amdgcn_readlane(g * V + bi, wl);
+      sel_v[j] = m;
+      sel_e[j] = we;
+      if (g == wl) {
+#pragma unroll
+        for (int i = 0; i < VMAX; ++i)
+          if (i == bi) taken[i] = true;
+      }
+    }
+  }
   if (live && g < k) {
     // softmax over the k selected logits (slot 0 holds the largest)
     const float m = sel_v[0];
@@ -476,7 +549,8 @@ __global__ __launch_bounds__(256) void route_topk_rows_kernel(const float* parti
       }
     }
   }
-  select_topk<64, VMAX, true>(val, taken, g, t, live, k, topk_ids, topk_w, V);
+  // live is uniform across the wave (one token per wave)
+  if (live) select_topk_wave<VMAX>(val, taken, g, t, true, k, V, topk_ids, topk_w);
 }
 
 // Few experts: one workgroup of 256 threads per token computes the logits directly. Thread i
@@ -543,7 +617,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(const TX* __restrict__
     s = s + 0.0f;                          // -0 -> +0
     val[0] = (s == s) ? s : -INFINITY;     // NaN ranks as -inf
   }
-  select_topk<64, 1>(val, taken, lane, t, true, k, topk_ids, topk_w);
+  select_topk_wave<1>(val, taken, lane, t, true, k, 1, topk_ids, topk_w);
 }
 
 }  // namespace
