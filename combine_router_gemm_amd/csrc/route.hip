@@ -347,6 +347,20 @@ __device__ __forceinline__ float wave_max(float x) {
   const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
+// Sum of x over the 64 lanes of the wave, in every lane, in a fixed order: pairs, quads, 8- and 16-lane
+// groups by DPP (each partner adds the same two values, so every lane of a row holds the same bits),
+// then (row 0 + row 1) + (row 2 + row 3).
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  x += dpp_f32<0x140>(x);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return (r0 + r1) + (r2 + r3);
+}
 
 // The selection of select_topk for one token per wave with lane g holding experts g * V + i (i < V): each
 // round takes every lane's best untaken value (the lowest i on ties), the wave maximum of those, and as
@@ -556,7 +570,7 @@ __global__ __launch_bounds__(256) void route_topk_rows_kernel(const float* parti
 // Few experts: one workgroup of 256 threads per token computes the logits directly. Thread i
 // accumulates in fp32 the products of the 16-byte x chunks i, i + 256, ... with the matching fp32
 // router-weight slices of every expert (all loads of a chunk in flight at once; the router weight is
-// an L2 hit after the first token), a butterfly sums each expert over the wave, and wave 0 adds the
+// an L2 hit after the first token), a DPP reduction sums each expert over the wave, and wave 0 adds the
 // four wave sums in wave order (deterministic). Lane e (< E) of wave 0 then holds logit e for the
 // same selection as route_topk.
 template <typename TX, int EMAX>
@@ -598,9 +612,7 @@ __global__ __launch_bounds__(256) void route_small_kernel(const TX* __restrict__
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) {
     if (e < E) {
-      float v = acc[e];
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      const float v = wave_sum(acc[e]);
       if (lane == 0) s_part[wave][e] = v;
     }
   }
