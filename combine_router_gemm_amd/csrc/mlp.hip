@@ -356,43 +356,265 @@ __global__ __launch_bounds__(256) void combine_prep_kernel(const int* __restrict
 // then the BN/2 up rows of the same output columns, and each wave owns matching gate and up
 // accumulators.
 template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
-          bool BUF, bool COMBINE = false>
-__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(MOE_GEMM_MIN_WAVES)))
-void mlp_gemm_kernel(GemmArgs args) {
-  static_assert(!COMBINE || !GATED, "the combine follows the down GEMM");
-  constexpr int NTH = WM * WN * 64;
-  constexpr int VN = Vec<T>::N;           // elements per 16-byte vector
-  constexpr int PAD = 16 / sizeof(T);     // one vector of padding per LDS row
-  constexpr int LDR = BK + PAD;           // LDS row length (elements)
-  constexpr int VPR = BK / VN;            // vectors per tile row per stage
-  constexpr int A_VEC = BM * VPR / NTH;   // A vectors loaded per thread per stage
-  constexpr int B_VEC = BN * VPR / NTH;
-  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-  constexpr int S = Op::S;
-  constexpr int TM = WTM / S;
-  constexpr int TN = GATED ? (BN / 2 / WN) / S : WTN / S;  // per half when gated
-  constexpr int NACC = GATED ? 2 * TN : TN;
-  constexpr int OUT_COLS = GATED ? BN / 2 : BN;  // output columns per tile
+          bool BUF, bool COMBINE>
+struct RegTile {
+  static constexpr int NTH = WM * WN * 64;
+  static constexpr int VN = Vec<T>::N;           // elements per 16-byte vector
+  static constexpr int PAD = 16 / sizeof(T);     // one vector of padding per LDS row
+  static constexpr int LDR = BK + PAD;           // LDS row length (elements)
+  static constexpr int VPR = BK / VN;            // vectors per tile row per stage
+  static constexpr int A_VEC = BM * VPR / NTH;   // A vectors loaded per thread per stage
+  static constexpr int B_VEC = BN * VPR / NTH;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+  static constexpr int S = Op::S;
+  static constexpr int TM = WTM / S;
+  static constexpr int TN = GATED ? (BN / 2 / WN) / S : WTN / S;  // per half when gated
+  static constexpr int NACC = GATED ? 2 * TN : TN;
+  static constexpr int OUT_COLS = GATED ? BN / 2 : BN;  // output columns per tile
   static_assert(BM * VPR % NTH == 0 && BN * VPR % NTH == 0, "loader must tile evenly");
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(BK % Op::KS == 0 && BK % 32 == 0, "BK must be a multiple of the MFMA K step");
   static_assert(TM * S == WTM && (GATED ? TN * S * WN * 2 == BN : TN * S == WTN), "wave tile must tile by S");
 
+  static_assert(LDB == 1 || LDB == 2, "one or two LDS stages");
+
+  // One tile: `tile` indexes the (local expert, N tile, M tile) list of the plan (row_start and
+  // tile_start hold its per-expert starts); As / Bs are the LDB LDS stages of A and B.
+  __device__ __forceinline__ static void run(const GemmArgs& args, int tile, const int* row_start,
+                                             const int* tile_start, T (*As)[BM * LDR], T (*Bs)[BN * LDR]) {
+    const T* __restrict__ A = static_cast<const T*>(args.A);
+    const T* __restrict__ W = static_cast<const T*>(args.W);
+    T* __restrict__ Out = static_cast<T*>(args.Out);
+    constexpr int A_OOB = 0x7ffffff0;
+    const __amdgpu_buffer_rsrc_t a_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, BUF ? args.a_bytes : 0, 0x00020000);
+    const int El = args.El;
+    const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+  // tile -> (local expert l, n tile, m tile): l is the last expert with tile_start[l]*n_tiles <= tile
+  int lo = 0, hi = El;  // invariant: tile_start[lo]*n_tiles <= tile < tile_start[hi]*n_tiles
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (tile_start[mid] * n_tiles <= tile) lo = mid;
+    else hi = mid;
+  }
+  const int l = lo;
+  const int mt_l = tile_start[l + 1] - tile_start[l];
+  const int local = tile - tile_start[l] * n_tiles;
+  const int nt = local / mt_l, mt = local % mt_l;
+  const int p0 = row_start[l] + mt * BM;
+  const int m_rows = min(BM, row_start[l + 1] - p0);
+  const int n0 = nt * OUT_COLS;
+  const T* Wl = W + (int64_t)l * args.w_stride;
+
+  // per-thread source rows (fixed for the whole K loop). Every load is issued unconditionally from a
+  // valid address (rows past the tile end read the tile's first row, columns past K read the last
+  // vector of the row) and masked to zero when it is written to LDS: a load under a branch would
+  // make the compiler wait for every load in flight before the registers are reused.
+  // BUF: A and W are read with buffer loads (32-bit offsets instead of 64-bit pointers), and rows
+  // past the tile or past N use an offset past the buffer, which the hardware answers with zeros and
+  // no memory request (a tile of an expert with few rows then moves only its real rows)
+  const T* a_src[A_VEC];
+  int a_off[A_VEC];
+  int a_lds[A_VEC];
+  bool a_ok[A_VEC];
+#pragma unroll
+  for (int i = 0; i < A_VEC; ++i) {
+    const int idx = tid + i * NTH;
+    const int r = idx / VPR, c = (idx % VPR) * VN;
+    a_lds[i] = r * LDR + c;
+    a_ok[i] = r < m_rows;
+    const int p = p0 + (a_ok[i] ? r : 0);
+    const int src_row = args.a_perm ? args.a_perm[p] : p;
+    a_src[i] = A + (int64_t)src_row * args.lda;
+    a_off[i] = (BUF && a_ok[i]) ? src_row * args.lda * (int)sizeof(T) : A_OOB;  // < a_bytes when BUF
+  }
+  const T* b_src[B_VEC];
+  int b_off[B_VEC];
+  int b_lds[B_VEC];
+  bool b_ok[B_VEC];
+  const __amdgpu_buffer_rsrc_t b_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Wl, (short)0, BUF ? args.w_bytes : 0, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < B_VEC; ++i) {
+    const int idx = tid + i * NTH;
+    const int r = idx / VPR, c = (idx % VPR) * VN;
+    b_lds[i] = r * LDR + c;
+    int wrow, ncol;
+    if (GATED) {
+      const int half = r / (BN / 2), rr = r % (BN / 2);
+      ncol = n0 + rr;
+      wrow = ncol + half * args.up_offset;
+    } else {
+      ncol = n0 + r;
+      wrow = ncol;
+    }
+    b_ok[i] = ncol < args.N;
+    b_src[i] = Wl + (int64_t)(b_ok[i] ? wrow : 0) * args.K;
+    b_off[i] = (BUF && b_ok[i]) ? wrow * args.K * (int)sizeof(T) : A_OOB;  // < w_bytes when BUF
+  }
+
+  typename Op::Acc acc[TM][NACC];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < NACC; ++j)
+#pragma unroll
+      for (int q = 0; q < Op::NR; ++q) acc[i][j][q] = 0.f;
+
+  // RS register stages of global loads in flight: stage s + RS is requested before the MFMAs of
+  // stage s run, and stage s + 1 moves from registers to LDS after them (one barrier per stage).
+  const int nk = (args.K + BK - 1) / BK;
+  const int rot = k_rotation(args.k_rotate, l, n_tiles, nt, nk);
+  // stage st of the loop reads K slice (st + rot) mod nk
+  auto kslice = [&](int st) { return (st + rot < nk ? st + rot : st + rot - nk) * BK; };
+  u32x4 ra[RS][A_VEC], rb[RS][B_VEC];
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto load_stage = [&](int st, u32x4 (&xa)[A_VEC], u32x4 (&xb)[B_VEC]) {
+    const int k0 = kslice(st);
+#pragma unroll
+    for (int i = 0; i < A_VEC; ++i) {
+      const int col = min(k0 + a_lds[i] % LDR, args.K - VN);
+      if (BUF) {
+        const int vo = a_off[i] == A_OOB ? A_OOB : a_off[i] + col * (int)sizeof(T);
+        xa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, vo, 0, 0));
+      } else {
+        xa[i] = ld16(a_src[i] + col);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_VEC; ++i) {
+      // weights are read once per tile: streaming (non-temporal) loads keep the reused activation
+      // rows resident in L2 when many tiles share them
+      const int col = min(k0 + b_lds[i] % LDR, args.K - VN);
+      if (BUF) {
+        const int vo = b_off[i] == A_OOB ? A_OOB : b_off[i] + col * (int)sizeof(T);
+        xb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, vo, 0, BNT ? 2 : 0));
+      } else {
+        const T* pb = b_src[i] + col;
+        xb[i] = BNT ? ld16_nt(pb) : ld16(pb);
+      }
+    }
+  };
+  auto store_stage = [&](int st, int buf, const u32x4 (&xa)[A_VEC], const u32x4 (&xb)[B_VEC]) {
+    const int k0 = kslice(st);
+#pragma unroll
+    for (int i = 0; i < A_VEC; ++i) {
+      st16(&As[buf][a_lds[i]], (a_ok[i] && k0 + a_lds[i] % LDR < args.K) ? xa[i] : zero);
+    }
+#pragma unroll
+    for (int i = 0; i < B_VEC; ++i) st16(&Bs[buf][b_lds[i]], (b_ok[i] && k0 + b_lds[i] % LDR < args.K) ? xb[i] : zero);
+  };
+  const int fr = lane % S;
+  const int fk = (lane / S) * 8;  // 8 consecutive K per lane inside each K step
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += Op::KS) {
+      u32x4 af[TM][Op::VPF];
+      u32x4 bfg[NACC][Op::VPF];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const T* pa = &As[buf][(wm * WTM + i * S + fr) * LDR + kk + fk];
+#pragma unroll
+        for (int q = 0; q < Op::VPF; ++q) af[i][q] = ld16(pa + q * VN);
+      }
+#pragma unroll
+      for (int j = 0; j < NACC; ++j) {
+        int brow;
+        if (GATED) {
+          const int half = j / TN, jj = j % TN;
+          brow = half * (BN / 2) + wn * (BN / 2 / WN) + jj * S + fr;
+        } else {
+          brow = wn * WTN + j * S + fr;
+        }
+        const T* pb = &Bs[buf][brow * LDR + kk + fk];
+#pragma unroll
+        for (int q = 0; q < Op::VPF; ++q) bfg[j][q] = ld16(pb + q * VN);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[i], bfg[j]);
+    }
+  };
+
+  // stages past the last one re-read the last stage (an L2 hit) so that no load sits under a branch
+#pragma unroll
+  for (int u = 0; u < RS; ++u) load_stage(min(u, nk - 1), ra[u], rb[u]);
+  if (LDB == 2) {
+    store_stage(0, 0, ra[0], rb[0]);
+    lds_barrier();
+  }
+  for (int s0 = 0; s0 < nk; s0 += RS) {
+#pragma unroll
+    for (int u = 0; u < RS; ++u) {
+      const int st = s0 + u;  // register slot u holds stage st
+      if (st < nk) {
+        if (LDB == 2) {  // stage st is already in LDS
+          load_stage(min(st + RS, nk - 1), ra[u], rb[u]);
+          compute(st & 1);
+          if (st + 1 < nk) store_stage(st + 1, (st + 1) & 1, ra[(u + 1) % RS], rb[(u + 1) % RS]);
+          lds_barrier();
+        } else {
+          lds_barrier();  // every wave is done reading the previous stage
+          store_stage(st, 0, ra[u], rb[u]);
+          lds_barrier();
+          load_stage(min(st + RS, nk - 1), ra[u], rb[u]);
+          compute(0);
+        }
+      }
+    }
+  }
+  if (LDB == 1) lds_barrier();  // the next tile overwrites the LDS stage
+
+  // epilogue: lane l holds column l % S of each S x S accumulator; Op::out_row gives the rows
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int cl = GATED ? wn * (BN / 2 / WN) + j * S + (lane % S) : wn * WTN + j * S + (lane % S);
+      const int col = n0 + cl;
+#pragma unroll
+      for (int q = 0; q < Op::NR; ++q) {
+        const int row = wm * WTM + i * S + Op::out_row(lane, q);
+        if (row < m_rows && col < args.N) {
+          float v;
+          if (GATED) v = silu_f32(acc[i][j][q]) * acc[i][j + TN][q];
+          else v = acc[i][j][q];
+          const int p = p0 + row;
+          const int orow = args.out_perm ? args.out_perm[p] : p;
+          if (COMBINE) st_agent(Out + (int64_t)orow * args.ldo + col, v);
+          else Out[(int64_t)orow * args.ldo + col] = from_f32<T>(v);
+        }
+      }
+    }
+  }
+  if (COMBINE) {
+    static_assert(BM * LDR * sizeof(T) >= (BM + 1) * sizeof(int), "token list must fit the A stage");
+    if (LDB == 2) lds_barrier();  // the last stage's fragments are read before As is reused
+    tile_arrive_combine<T, NTH, OUT_COLS>(args, p0, m_rows, n0, nt, n_tiles, reinterpret_cast<int*>(&As[0][0]));
+  }
+  }
+};
+
+template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
+          bool BUF, bool COMBINE = false>
+__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(MOE_GEMM_MIN_WAVES)))
+void mlp_gemm_kernel(GemmArgs args) {
+  static_assert(!COMBINE || !GATED, "the combine follows the down GEMM");
+  using Tile = RegTile<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, BUF, COMBINE>;
+  constexpr int NTH = Tile::NTH, LDR = Tile::LDR;
   // LDB = 2: two LDS stages, the MFMAs read one while the next stage is written into the other (one
   // barrier per stage). LDB = 1: one LDS stage and two barriers per stage, half the LDS, so more
   // workgroups fit on a CU; the RS register stages keep the global loads in flight either way.
-  static_assert(LDB == 1 || LDB == 2, "one or two LDS stages");
   __shared__ __attribute__((aligned(16))) T As[LDB][BM * LDR];
   __shared__ __attribute__((aligned(16))) T Bs[LDB][BN * LDR];
 
-  const T* __restrict__ A = static_cast<const T*>(args.A);
-  const T* __restrict__ W = static_cast<const T*>(args.W);
-  T* __restrict__ Out = static_cast<T*>(args.Out);
-  constexpr int A_OOB = 0x7ffffff0;
-  const __amdgpu_buffer_rsrc_t a_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, BUF ? args.a_bytes : 0, 0x00020000);
   const int El = args.El;
-  const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
+  const int n_tiles = (args.N + Tile::OUT_COLS - 1) / Tile::OUT_COLS;
   const int total = args.plan[0] * n_tiles;
 
   const int tid = threadIdx.x;
@@ -406,9 +628,6 @@ void mlp_gemm_kernel(GemmArgs args) {
     tile_start[i] = args.plan[3 + El + i];
   }
   __syncthreads();
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
 
   // XCD-aware order: workgroup b runs on XCD b % 8. The tile list is cut into 8 near-equal contiguous
   // ranges, one per XCD (neighbouring tiles share operands in that XCD's L2), and the XCD's
@@ -421,212 +640,7 @@ void mlp_gemm_kernel(GemmArgs args) {
     t_end = min(total, (x + 1) * per);
     t_step = G >> 3;
   }
-
-  for (int tile = t_begin; tile < t_end; tile += t_step) {
-    // tile -> (local expert l, n tile, m tile): l is the last expert with tile_start[l]*n_tiles <= tile
-    int lo = 0, hi = El;  // invariant: tile_start[lo]*n_tiles <= tile < tile_start[hi]*n_tiles
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tile_start[mid] * n_tiles <= tile) lo = mid;
-      else hi = mid;
-    }
-    const int l = lo;
-    const int mt_l = tile_start[l + 1] - tile_start[l];
-    const int local = tile - tile_start[l] * n_tiles;
-    const int nt = local / mt_l, mt = local % mt_l;
-    const int p0 = row_start[l] + mt * BM;
-    const int m_rows = min(BM, row_start[l + 1] - p0);
-    const int n0 = nt * OUT_COLS;
-    const T* Wl = W + (int64_t)l * args.w_stride;
-
-    // per-thread source rows (fixed for the whole K loop). Every load is issued unconditionally from a
-    // valid address (rows past the tile end read the tile's first row, columns past K read the last
-    // vector of the row) and masked to zero when it is written to LDS: a load under a branch would
-    // make the compiler wait for every load in flight before the registers are reused.
-    // BUF: A and W are read with buffer loads (32-bit offsets instead of 64-bit pointers), and rows
-    // past the tile or past N use an offset past the buffer, which the hardware answers with zeros and
-    // no memory request (a tile of an expert with few rows then moves only its real rows)
-    const T* a_src[A_VEC];
-    int a_off[A_VEC];
-    int a_lds[A_VEC];
-    bool a_ok[A_VEC];
-#pragma unroll
-    for (int i = 0; i < A_VEC; ++i) {
-      const int idx = tid + i * NTH;
-      const int r = idx / VPR, c = (idx % VPR) * VN;
-      a_lds[i] = r * LDR + c;
-      a_ok[i] = r < m_rows;
-      const int p = p0 + (a_ok[i] ? r : 0);
-      const int src_row = args.a_perm ? args.a_perm[p] : p;
-      a_src[i] = A + (int64_t)src_row * args.lda;
-      a_off[i] = (BUF && a_ok[i]) ? src_row * args.lda * (int)sizeof(T) : A_OOB;  // < a_bytes when BUF
-    }
-    const T* b_src[B_VEC];
-    int b_off[B_VEC];
-    int b_lds[B_VEC];
-    bool b_ok[B_VEC];
-    const __amdgpu_buffer_rsrc_t b_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Wl, (short)0, BUF ? args.w_bytes : 0, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < B_VEC; ++i) {
-      const int idx = tid + i * NTH;
-      const int r = idx / VPR, c = (idx % VPR) * VN;
-      b_lds[i] = r * LDR + c;
-      int wrow, ncol;
-      if (GATED) {
-        const int half = r / (BN / 2), rr = r % (BN / 2);
-        ncol = n0 + rr;
-        wrow = ncol + half * args.up_offset;
-      } else {
-        ncol = n0 + r;
-        wrow = ncol;
-      }
-      b_ok[i] = ncol < args.N;
-      b_src[i] = Wl + (int64_t)(b_ok[i] ? wrow : 0) * args.K;
-      b_off[i] = (BUF && b_ok[i]) ? wrow * args.K * (int)sizeof(T) : A_OOB;  // < w_bytes when BUF
-    }
-
-    typename Op::Acc acc[TM][NACC];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < NACC; ++j)
-#pragma unroll
-        for (int q = 0; q < Op::NR; ++q) acc[i][j][q] = 0.f;
-
-    // RS register stages of global loads in flight: stage s + RS is requested before the MFMAs of
-    // stage s run, and stage s + 1 moves from registers to LDS after them (one barrier per stage).
-    const int nk = (args.K + BK - 1) / BK;
-    const int rot = k_rotation(args.k_rotate, l, n_tiles, nt, nk);
-    // stage st of the loop reads K slice (st + rot) mod nk
-    auto kslice = [&](int st) { return (st + rot < nk ? st + rot : st + rot - nk) * BK; };
-    u32x4 ra[RS][A_VEC], rb[RS][B_VEC];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    auto load_stage = [&](int st, u32x4 (&xa)[A_VEC], u32x4 (&xb)[B_VEC]) {
-      const int k0 = kslice(st);
-#pragma unroll
-      for (int i = 0; i < A_VEC; ++i) {
-        const int col = min(k0 + a_lds[i] % LDR, args.K - VN);
-        if (BUF) {
-          const int vo = a_off[i] == A_OOB ? A_OOB : a_off[i] + col * (int)sizeof(T);
-          xa[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, vo, 0, 0));
-        } else {
-          xa[i] = ld16(a_src[i] + col);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < B_VEC; ++i) {
-        // weights are read once per tile: streaming (non-temporal) loads keep the reused activation
-        // rows resident in L2 when many tiles share them
-        const int col = min(k0 + b_lds[i] % LDR, args.K - VN);
-        if (BUF) {
-          const int vo = b_off[i] == A_OOB ? A_OOB : b_off[i] + col * (int)sizeof(T);
-          xb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc, vo, 0, BNT ? 2 : 0));
-        } else {
-          const T* pb = b_src[i] + col;
-          xb[i] = BNT ? ld16_nt(pb) : ld16(pb);
-        }
-      }
-    };
-    auto store_stage = [&](int st, int buf, const u32x4 (&xa)[A_VEC], const u32x4 (&xb)[B_VEC]) {
-      const int k0 = kslice(st);
-#pragma unroll
-      for (int i = 0; i < A_VEC; ++i) {
-        st16(&As[buf][a_lds[i]], (a_ok[i] && k0 + a_lds[i] % LDR < args.K) ? xa[i] : zero);
-      }
-#pragma unroll
-      for (int i = 0; i < B_VEC; ++i) st16(&Bs[buf][b_lds[i]], (b_ok[i] && k0 + b_lds[i] % LDR < args.K) ? xb[i] : zero);
-    };
-    const int fr = lane % S;
-    const int fk = (lane / S) * 8;  // 8 consecutive K per lane inside each K step
-    auto compute = [&](int buf) {
-#pragma unroll
-      for (int kk = 0; kk < BK; kk += Op::KS) {
-        u32x4 af[TM][Op::VPF];
-        u32x4 bfg[NACC][Op::VPF];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const T* pa = &As[buf][(wm * WTM + i * S + fr) * LDR + kk + fk];
-#pragma unroll
-          for (int q = 0; q < Op::VPF; ++q) af[i][q] = ld16(pa + q * VN);
-        }
-#pragma unroll
-        for (int j = 0; j < NACC; ++j) {
-          int brow;
-          if (GATED) {
-            const int half = j / TN, jj = j % TN;
-            brow = half * (BN / 2) + wn * (BN / 2 / WN) + jj * S + fr;
-          } else {
-            brow = wn * WTN + j * S + fr;
-          }
-          const T* pb = &Bs[buf][brow * LDR + kk + fk];
-#pragma unroll
-          for (int q = 0; q < Op::VPF; ++q) bfg[j][q] = ld16(pb + q * VN);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[i], bfg[j]);
-      }
-    };
-
-    // stages past the last one re-read the last stage (an L2 hit) so that no load sits under a branch
-#pragma unroll
-    for (int u = 0; u < RS; ++u) load_stage(min(u, nk - 1), ra[u], rb[u]);
-    if (LDB == 2) {
-      store_stage(0, 0, ra[0], rb[0]);
-      lds_barrier();
-    }
-    for (int s0 = 0; s0 < nk; s0 += RS) {
-#pragma unroll
-      for (int u = 0; u < RS; ++u) {
-        const int st = s0 + u;  // register slot u holds stage st
-        if (st < nk) {
-          if (LDB == 2) {  // stage st is already in LDS
-            load_stage(min(st + RS, nk - 1), ra[u], rb[u]);
-            compute(st & 1);
-            if (st + 1 < nk) store_stage(st + 1, (st + 1) & 1, ra[(u + 1) % RS], rb[(u + 1) % RS]);
-            lds_barrier();
-          } else {
-            lds_barrier();  // every wave is done reading the previous stage
-            store_stage(st, 0, ra[u], rb[u]);
-            lds_barrier();
-            load_stage(min(st + RS, nk - 1), ra[u], rb[u]);
-            compute(0);
-          }
-        }
-      }
-    }
-    if (LDB == 1) lds_barrier();  // the next tile overwrites the LDS stage
-
-    // epilogue: lane l holds column l % S of each S x S accumulator; Op::out_row gives the rows
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int cl = GATED ? wn * (BN / 2 / WN) + j * S + (lane % S) : wn * WTN + j * S + (lane % S);
-        const int col = n0 + cl;
-#pragma unroll
-        for (int q = 0; q < Op::NR; ++q) {
-          const int row = wm * WTM + i * S + Op::out_row(lane, q);
-          if (row < m_rows && col < args.N) {
-            float v;
-            if (GATED) v = silu_f32(acc[i][j][q]) * acc[i][j + TN][q];
-            else v = acc[i][j][q];
-            const int p = p0 + row;
-            const int orow = args.out_perm ? args.out_perm[p] : p;
-            if (COMBINE) st_agent(Out + (int64_t)orow * args.ldo + col, v);
-            else Out[(int64_t)orow * args.ldo + col] = from_f32<T>(v);
-          }
-        }
-      }
-    }
-    if (COMBINE) {
-      static_assert(BM * LDR * sizeof(T) >= (BM + 1) * sizeof(int), "token list must fit the A stage");
-      if (LDB == 2) lds_barrier();  // the last stage's fragments are read before As is reused
-      tile_arrive_combine<T, NTH, OUT_COLS>(args, p0, m_rows, n0, nt, n_tiles, reinterpret_cast<int*>(&As[0][0]));
-    }
-  }
+  for (int tile = t_begin; tile < t_end; tile += t_step) Tile::run(args, tile, row_start, tile_start, As, Bs);
 }
 
 // ------------------------------------------------------------------------------------------------
