@@ -54,33 +54,25 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wsum, int* tot
   return wbase + incl - v;
 }
 
-// SCAN (one block, T <= DISPATCH_TB): the block is the whole batch, so its per-expert bases are 0 and
-// the block also writes count / kept / overflow and the expert offsets, in place of dispatch_scan.
-template <bool SCAN>
-__global__ __launch_bounds__(DR_THREADS) void dispatch_rank_kernel(const int* __restrict__ ids, int T, int k,
-                                                                  int E, int* __restrict__ blk_count,
-                                                                  int* __restrict__ pair_local, int C,
-                                                                  int* __restrict__ count, int* __restrict__ kept,
-                                                                  int* __restrict__ overflow,
-                                                                  int* __restrict__ offset) {
-  __shared__ int cnt[DR_WAVES][MOE_MAX_EXPERTS];
-  __shared__ int s_tot[SCAN ? MOE_MAX_EXPERTS : 1];
-  __shared__ int s_wsum[DR_WAVES];
+// Stable ranks of the pairs [p_begin, p_end) of one workgroup of DR_THREADS threads. Wave w takes the
+// 64 k pairs from p_begin + 64 k w in k chunks of 64; lanes with the same expert find each other with one
+// ballot per id bit (a wave-wide match), which gives the stable rank inside the 64, and one lane per
+// distinct expert does an LDS atomic add of the group size on a wave-private counter (per-wave counters
+// keep the order stable). On return (after a barrier) cnt[w][e] holds wave w's base for expert e inside
+// the workgroup and tot[e] the workgroup's count of expert e; lane chunk c's pair (p = w_begin + 64 c +
+// lane) has expert mye[c] (-1: no pair, or an id out of range) and rank myrank[c] in its wave.
+__device__ __forceinline__ void rank_pairs(const int* __restrict__ ids, int64_t p_begin, int64_t p_end, int k, int E,
+                                           int (*cnt)[MOE_MAX_EXPERTS], int* tot, int (&myrank)[MOE_MAX_TOPK],
+                                           int (&mye)[MOE_MAX_TOPK], int64_t& w_begin) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   for (int i = tid; i < DR_WAVES * E; i += DR_THREADS) cnt[i / E][i % E] = 0;
   __syncthreads();
-
-  const int64_t p_begin = (int64_t)blockIdx.x * DISPATCH_TB * k;
-  const int64_t p_end = min((int64_t)(blockIdx.x + 1) * DISPATCH_TB, (int64_t)T) * k;
   // each wave takes DISPATCH_TB * k / DR_WAVES = 64 * k consecutive pairs: k chunks of 64
-  const int64_t w_begin = p_begin + (int64_t)wave * 64 * k;
+  w_begin = p_begin + (int64_t)wave * 64 * k;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
-
-  int myrank[MOE_MAX_TOPK];
-  int mye[MOE_MAX_TOPK];
   // the ids of all k chunks in flight together, before the first ballot waits on one
   int ide[MOE_MAX_TOPK];
 #pragma unroll
@@ -115,7 +107,7 @@ __global__ __launch_bounds__(DR_THREADS) void dispatch_rank_kernel(const int* __
     }
   }
   __syncthreads();
-  // exclusive scan over the waves (pair order), per expert; the block total is the histogram row
+  // exclusive scan over the waves (pair order), per expert; the workgroup total is the histogram row
   for (int e = tid; e < E; e += DR_THREADS) {
     int acc = 0;
 #pragma unroll
@@ -124,35 +116,65 @@ __global__ __launch_bounds__(DR_THREADS) void dispatch_rank_kernel(const int* __
       cnt[w][e] = acc;
       acc += c;
     }
-    if (SCAN) {
-      blk_count[e] = 0;
-      s_tot[e] = acc;
-    } else {
-      blk_count[(int64_t)blockIdx.x * E + e] = acc;
-    }
+    tot[e] = acc;
   }
   __syncthreads();
-  if (SCAN) {
-    // thread i owns experts 2i and 2i + 1 (E <= 2 * DR_THREADS)
-    const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
-    const int k0 = e0 < E ? min(s_tot[e0], C) : 0;
-    const int k1 = e1 < E ? min(s_tot[e1], C) : 0;
-    int total = 0;
-    const int excl = block_exclusive_scan(k0 + k1, s_wsum, &total);
-    if (e0 < E) {
-      count[e0] = s_tot[e0];
-      kept[e0] = k0;
-      overflow[e0] = s_tot[e0] - k0;
-      offset[e0] = excl;
-    }
-    if (e1 < E) {
-      count[e1] = s_tot[e1];
-      kept[e1] = k1;
-      overflow[e1] = s_tot[e1] - k1;
-      offset[e1] = excl + k0;
-    }
-    if (threadIdx.x == 0) offset[E] = total;
+}
+
+// Counts of the whole batch (one workgroup, T <= DISPATCH_TB): count / kept / overflow, and the offsets
+// (an exclusive scan of kept over experts; thread i owns experts 2i and 2i + 1, E <= 2 * DR_THREADS),
+// also into s_off when non-null. write: store them to the layout.
+__device__ __forceinline__ void batch_offsets(const int* tot, int E, int C, int* s_wsum, int* s_off, bool write,
+                                              int* __restrict__ count, int* __restrict__ kept,
+                                              int* __restrict__ overflow, int* __restrict__ offset) {
+  const int e0 = 2 * threadIdx.x, e1 = e0 + 1;
+  const int k0 = e0 < E ? min(tot[e0], C) : 0;
+  const int k1 = e1 < E ? min(tot[e1], C) : 0;
+  int total = 0;
+  const int excl = block_exclusive_scan(k0 + k1, s_wsum, &total);
+  if (s_off) {
+    if (e0 < E) s_off[e0] = excl;
+    if (e1 < E) s_off[e1] = excl + k0;
   }
+  if (!write) return;
+  if (e0 < E) {
+    count[e0] = tot[e0];
+    kept[e0] = k0;
+    overflow[e0] = tot[e0] - k0;
+    offset[e0] = excl;
+  }
+  if (e1 < E) {
+    count[e1] = tot[e1];
+    kept[e1] = k1;
+    overflow[e1] = tot[e1] - k1;
+    offset[e1] = excl + k0;
+  }
+  if (threadIdx.x == 0) offset[E] = total;
+}
+
+// One workgroup per DISPATCH_TB tokens: the ranks of its pairs (to pair_local) and its histogram row (to
+// blk_count). SCAN (one block, T <= DISPATCH_TB): the block is the whole batch, so its per-expert bases
+// are 0 and the block also writes count / kept / overflow and the expert offsets, in place of
+// dispatch_scan.
+template <bool SCAN>
+__global__ __launch_bounds__(DR_THREADS) void dispatch_rank_kernel(const int* __restrict__ ids, int T, int k,
+                                                                  int E, int* __restrict__ blk_count,
+                                                                  int* __restrict__ pair_local, int C,
+                                                                  int* __restrict__ count, int* __restrict__ kept,
+                                                                  int* __restrict__ overflow,
+                                                                  int* __restrict__ offset) {
+  __shared__ int cnt[DR_WAVES][MOE_MAX_EXPERTS];
+  __shared__ int s_tot[MOE_MAX_EXPERTS];
+  __shared__ int s_wsum[DR_WAVES];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t p_begin = (int64_t)blockIdx.x * DISPATCH_TB * k;
+  const int64_t p_end = min((int64_t)(blockIdx.x + 1) * DISPATCH_TB, (int64_t)T) * k;
+  int myrank[MOE_MAX_TOPK], mye[MOE_MAX_TOPK];
+  int64_t w_begin;
+  rank_pairs(ids, p_begin, p_end, k, E, cnt, s_tot, myrank, mye, w_begin);
+  for (int e = threadIdx.x; e < E; e += DR_THREADS) blk_count[(int64_t)(SCAN ? 0 : blockIdx.x) * E + e] = SCAN ? 0 : s_tot[e];
+  if (SCAN) batch_offsets(s_tot, E, C, s_wsum, nullptr, true, count, kept, overflow, offset);
 #pragma unroll
   for (int c = 0; c < MOE_MAX_TOPK; ++c) {
     if (c < k) {
@@ -243,15 +265,12 @@ __device__ __forceinline__ int resolve_pair_row(int t, int lane, const int* __re
   return row;
 }
 
+// One wave copies token row t of x to the kept rows (lane j < k holds the row of pair (t, j), -1 if
+// dropped): VPL 16-byte slices per lane in flight, each read once and stored to every kept row.
 template <typename T, int VPL>
-__global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_kernel(
-    const T* __restrict__ x, const int* __restrict__ ids, int T_, int H, int k, int E, int C,
-    const int* __restrict__ blk_base, const int* __restrict__ pair_local, const int* __restrict__ offset,
-    int* __restrict__ row_token, int* __restrict__ row_slot, int* __restrict__ pair_row, T* __restrict__ send_buf) {
+__device__ __forceinline__ void copy_token_row(const T* __restrict__ x, int t, int H, int row,
+                                               T* __restrict__ send_buf) {
   const int lane = lane_id();
-  const int t = blockIdx.x * SCATTER_WAVES + (int)(threadIdx.x >> 6);
-  if (t >= T_) return;
-  const int row = resolve_pair_row(t, lane, ids, k, E, C, blk_base, pair_local, offset, row_token, row_slot, pair_row);
   uint64_t kept = __ballot(row >= 0);  // only lanes < k can hold a row
   if (kept == 0) return;               // every pair of this token was dropped: nothing to copy
   constexpr int VN = Vec<T>::N;
@@ -274,6 +293,68 @@ __global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_kernel(
       }
     }
   }
+}
+
+template <typename T, int VPL>
+__global__ __launch_bounds__(SCATTER_WAVES * 64) void dispatch_scatter_kernel(
+    const T* __restrict__ x, const int* __restrict__ ids, int T_, int H, int k, int E, int C,
+    const int* __restrict__ blk_base, const int* __restrict__ pair_local, const int* __restrict__ offset,
+    int* __restrict__ row_token, int* __restrict__ row_slot, int* __restrict__ pair_row, T* __restrict__ send_buf) {
+  const int t = blockIdx.x * SCATTER_WAVES + (int)(threadIdx.x >> 6);
+  if (t >= T_) return;
+  const int row =
+      resolve_pair_row(t, lane_id(), ids, k, E, C, blk_base, pair_local, offset, row_token, row_slot, pair_row);
+  copy_token_row<T, VPL>(x, t, H, row, send_buf);
+}
+
+// The whole dispatch in one launch for a batch of at most DISPATCH_TB tokens: every workgroup ranks all
+// pairs and scans the counts itself (the work of the one-block dispatch_rank, repeated per workgroup, in
+// LDS), workgroup 0 writes count / kept / overflow / offsets, and then each wave scatters one token as
+// dispatch_scatter does. This saves a launch and its dependent global round trips on decode batches.
+template <typename T, int VPL>
+__global__ __launch_bounds__(DR_THREADS) void dispatch_small_kernel(
+    const T* __restrict__ x, const int* __restrict__ ids, int T_, int H, int k, int E, int C, int* __restrict__ count,
+    int* __restrict__ kept, int* __restrict__ overflow, int* __restrict__ offset, int* __restrict__ row_token,
+    int* __restrict__ row_slot, int* __restrict__ pair_row, T* __restrict__ send_buf) {
+  static_assert(DR_THREADS == SCATTER_WAVES * 64, "one wave per token");
+  __shared__ int cnt[DR_WAVES][MOE_MAX_EXPERTS];
+  __shared__ int s_tot[MOE_MAX_EXPERTS];
+  __shared__ int s_off[MOE_MAX_EXPERTS];
+  __shared__ int s_wsum[DR_WAVES];
+  __shared__ int s_pos[DISPATCH_TB * MOE_MAX_TOPK];  // pair -> position in its expert, -1: no expert
+  __shared__ int s_exp[DISPATCH_TB * MOE_MAX_TOPK];  // pair -> expert, -1: out of range
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t n_pairs = (int64_t)T_ * k;
+  int myrank[MOE_MAX_TOPK], mye[MOE_MAX_TOPK];
+  int64_t w_begin;
+  rank_pairs(ids, 0, n_pairs, k, E, cnt, s_tot, myrank, mye, w_begin);
+  batch_offsets(s_tot, E, C, s_wsum, s_off, blockIdx.x == 0, count, kept, overflow, offset);
+#pragma unroll
+  for (int c = 0; c < MOE_MAX_TOPK; ++c) {
+    if (c < k) {
+      const int64_t p = w_begin + (int64_t)c * 64 + lane;
+      if (p < n_pairs) {
+        s_pos[p] = mye[c] >= 0 ? cnt[wave][mye[c]] + myrank[c] : -1;
+        s_exp[p] = mye[c];
+      }
+    }
+  }
+  __syncthreads();
+  const int t = blockIdx.x * SCATTER_WAVES + wave;
+  if (t >= T_) return;
+  int row = -1;
+  if (lane < k) {
+    const int p = t * k + lane;
+    const int e = s_exp[p], pos = s_pos[p];
+    if (e >= 0 && pos < C) row = s_off[e] + pos;
+    pair_row[p] = row;
+    if (row >= 0) {
+      row_token[row] = t;
+      row_slot[row] = lane;
+    }
+  }
+  copy_token_row<T, VPL>(x, t, H, row, send_buf);
 }
 
 template <typename T, int VPL>
@@ -395,11 +476,29 @@ static hipError_t launch_counts(const int* ids, const moe_layout_t& L, int* blk_
 
 hipError_t launch_dispatch(const void* x, int xdt_bf16, const int* ids, const moe_layout_t& L, void* send_buf,
                            int* blk_count, int* pair_local, hipStream_t stream) {
-  const hipError_t st = launch_counts(ids, L, blk_count, pair_local, stream);
-  if (st != hipSuccess || L.T == 0) return st;
   // slices per lane in flight: enough for the whole row in one pass up to 1024 slices (bf16 H <= 8192)
   const int nvec = L.H / (xdt_bf16 ? 8 : 4);
   const int vpl = nvec > 256 ? 16 : (nvec > 64 ? 4 : 1);
+  if (L.T > 0 && dispatch_num_blocks(L.T) == 1) {  // one launch: every workgroup ranks the whole batch
+    const unsigned blocks = (unsigned)ceil_div_host(L.T, SCATTER_WAVES);
+#define MOE_DISPATCH_SMALL(TY, VPL)                                                                         \
+  dispatch_small_kernel<TY, VPL><<<blocks, DR_THREADS, 0, stream>>>(                                         \
+      static_cast<const TY*>(x), ids, L.T, L.H, L.k, L.E, L.C, L.expert_count, L.expert_kept, L.expert_overflow, \
+      L.expert_offset, L.row_token, L.row_slot, L.pair_row, static_cast<TY*>(send_buf))
+    if (xdt_bf16) {
+      if (vpl == 16) MOE_DISPATCH_SMALL(bf16_t, 16);
+      else if (vpl == 4) MOE_DISPATCH_SMALL(bf16_t, 4);
+      else MOE_DISPATCH_SMALL(bf16_t, 1);
+    } else {
+      if (vpl == 16) MOE_DISPATCH_SMALL(float, 16);
+      else if (vpl == 4) MOE_DISPATCH_SMALL(float, 4);
+      else MOE_DISPATCH_SMALL(float, 1);
+    }
+#undef MOE_DISPATCH_SMALL
+    return hipGetLastError();
+  }
+  const hipError_t st = launch_counts(ids, L, blk_count, pair_local, stream);
+  if (st != hipSuccess || L.T == 0) return st;
   if (xdt_bf16) {
     if (vpl == 16) launch_scatter_t<bf16_t, 16>(x, ids, L, send_buf, blk_count, pair_local, stream);
     else if (vpl == 4) launch_scatter_t<bf16_t, 4>(x, ids, L, send_buf, blk_count, pair_local, stream);
