@@ -162,7 +162,8 @@ struct GemmArgs {
   void* Out;
   int ldo;
   const int* out_perm;  // scatter map for output rows (down) or nullptr (plan order)
-  const int* plan;
+  const int* plan;       // the plan kernel's output, or nullptr: build the plan from `offset` (R = 1)
+  const int* offset;     // [E + 1] the layout's expert offsets (used when plan is nullptr)
   int El;
   int a_bytes;          // bytes of A (rows_max x lda elements) when it fits 31-bit buffer offsets, else 0
   int w_bytes;          // bytes of one expert's weights (w_stride elements), same rule
@@ -240,6 +241,64 @@ __device__ __forceinline__ int k_rotation(int on, int l, int n_tiles, int nt, in
   return on ? (int)(((int64_t)l * n_tiles + nt) * MOE_K_ROT_STRIDE % nk) : 0;
 }
 inline int k_rotate_for(int K, int elem_bytes) { return MOE_K_ROTATE && ((int64_t)K * elem_bytes) % 4096 == 0; }
+
+// The plan's per-expert row and M-tile starts in LDS (row_start[0..El], tile_start[0..El]), by every
+// workgroup of NTH threads; returns the number of M tiles. With a plan they are copied from it. Without
+// one (one rank: the send rows are already grouped by expert, so plan order is send order and the row
+// map is the identity) they are built from the layout's expert offsets: row_start = offset and
+// tile_start = the exclusive scan of ceil(rows / BM), each thread taking a run of consecutive experts.
+template <int NTH>
+__device__ __forceinline__ int load_plan(const GemmArgs& args, int BM, int* row_start, int* tile_start) {
+  static_assert(NTH % 64 == 0 && NTH <= 1024, "whole waves");
+  const int El = args.El, tid = threadIdx.x;
+  if (args.plan) {
+    for (int i = tid; i <= El; i += NTH) {
+      row_start[i] = args.plan[2 + i];
+      tile_start[i] = args.plan[3 + El + i];
+    }
+    __syncthreads();
+    return args.plan[0];
+  }
+  __shared__ int s_wsum[NTH / 64];
+  const int lane = tid & 63, wave = tid >> 6;
+  const int per = (El + NTH - 1) / NTH, e0 = tid * per;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < El) {
+      const int a = args.offset[e];
+      row_start[e] = a;
+      sum += (args.offset[e + 1] - a + BM - 1) / BM;
+    }
+  }
+  int incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - sum, total = 0;
+#pragma unroll
+  for (int w = 0; w < NTH / 64; ++w) {
+    if (w < wave) run += s_wsum[w];
+    total += s_wsum[w];
+  }
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < El) {
+      tile_start[e] = run;
+      run += (args.offset[e + 1] - row_start[e] + BM - 1) / BM;
+    }
+  }
+  if (tid == 0) {
+    row_start[El] = args.offset[El];
+    tile_start[El] = total;
+  }
+  __syncthreads();
+  return total;
+}
 
 // ---- the combine fused into the down GEMM ----
 // Expert-output rows that another tile combines travel through agent-scope (sc1) loads and stores: they
@@ -613,21 +672,13 @@ void mlp_gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) T As[LDB][BM * LDR];
   __shared__ __attribute__((aligned(16))) T Bs[LDB][BN * LDR];
 
-  const int El = args.El;
   const int n_tiles = (args.N + Tile::OUT_COLS - 1) / Tile::OUT_COLS;
-  const int total = args.plan[0] * n_tiles;
-
-  const int tid = threadIdx.x;
-  // the plan's row and tile starts, copied to LDS once: every tile start then resolves its expert
-  // with LDS reads instead of a chain of dependent global loads
+  // the plan's row and tile starts in LDS: every tile start then resolves its expert with LDS reads
+  // instead of a chain of dependent global loads
   __shared__ int s_plan[2 * (MOE_MAX_EXPERTS + 1)];
   int* row_start = s_plan;
   int* tile_start = s_plan + MOE_MAX_EXPERTS + 1;
-  for (int i = tid; i <= El; i += NTH) {
-    row_start[i] = args.plan[2 + i];
-    tile_start[i] = args.plan[3 + El + i];
-  }
-  __syncthreads();
+  const int total = load_plan<NTH>(args, BM, row_start, tile_start) * n_tiles;
 
   // XCD-aware order: workgroup b runs on XCD b % 8. The tile list is cut into 8 near-equal contiguous
   // ranges, one per XCD (neighbouring tiles share operands in that XCD's L2), and the XCD's
@@ -692,6 +743,8 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
   const bf16_t* W = static_cast<const bf16_t*>(args.W);
   bf16_t* __restrict__ Out = static_cast<bf16_t*>(args.Out);
   const int El = args.El;
+  // the plan kernel's output (scalar loads: the plan is the same for the whole workgroup); this kernel
+  // always runs with a plan (an LDS copy measured 15 % to 2x slower here)
   const int* row_start = args.plan + 2;
   const int* tile_start = args.plan + 3 + El;
   const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
@@ -1151,16 +1204,22 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   const int El = L.E / L.R;
   const int H = L.H;
   const int64_t rows_max = moe_rows_max(L.T, L.k, L.E, L.C);
-  const int plan_blocks = (int)(rows_max > 0 ? ceil_div_host64(rows_max, PLAN_ROWS_PER_WG) : 1);
-  mlp_plan_kernel<<<plan_blocks, PLAN_THREADS, 0, stream>>>(L.expert_kept, L.expert_offset, L.E, El, tiles.BM, plan,
-                                                            perm);
+  // with one rank the send rows are already grouped by local expert: the register-staged GEMMs build the
+  // plan's starts from the expert offsets themselves and read rows in send order, with no plan launch
+  // (the direct-to-LDS kernels always read the plan kernel's output)
+  const bool own_plan = L.R > 1 || tiles.variant == 3 || tiles.variant == 4;
+  if (own_plan) {
+    const int plan_blocks = (int)(rows_max > 0 ? ceil_div_host64(rows_max, PLAN_ROWS_PER_WG) : 1);
+    mlp_plan_kernel<<<plan_blocks, PLAN_THREADS, 0, stream>>>(L.expert_kept, L.expert_offset, L.E, El, tiles.BM,
+                                                              plan, perm);
+  }
 
   const int64_t max_mtiles = ceil_div_host64(rows_max, tiles.BM) + El;
 
   GemmArgs gu{};
   gu.A = send_buf;
   gu.lda = H;
-  gu.a_perm = perm;
+  gu.a_perm = own_plan ? perm : nullptr;
   gu.W = w_gate_up;
   gu.w_stride = (int64_t)2 * F * H;
   gu.K = H;
@@ -1169,7 +1228,8 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   gu.Out = hbuf;
   gu.ldo = F;
   gu.out_perm = nullptr;
-  gu.plan = plan;
+  gu.plan = own_plan ? plan : nullptr;
+  gu.offset = L.expert_offset;
   gu.El = El;
   gu.a_bytes = buffer_bytes(rows_max * H * (xdt_bf16 ? 2 : 4));
   gu.w_bytes = buffer_bytes(gu.w_stride * (xdt_bf16 ? 2 : 4));
@@ -1186,8 +1246,9 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   dn.up_offset = 0;
   dn.Out = out_buf;
   dn.ldo = H;
-  dn.out_perm = perm;
-  dn.plan = plan;
+  dn.out_perm = own_plan ? perm : nullptr;
+  dn.plan = own_plan ? plan : nullptr;
+  dn.offset = L.expert_offset;
   dn.El = El;
   dn.a_bytes = buffer_bytes(rows_max * F * (xdt_bf16 ? 2 : 4));
   dn.w_bytes = buffer_bytes(dn.w_stride * (xdt_bf16 ? 2 : 4));
