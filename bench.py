@@ -383,8 +383,9 @@ def main():
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
     roof["traffic"] = None if (fp8 or fused) else measured_traffic(cfg.name)
     roof["kernel"] = ("moe_expert_mlp_fp8" if fp8 else ("moe_expert_mlp_combine" if fused else "moe_expert_mlp")) + \
-        (" (grouped GEMM: plan + counter clear + gate/up + down-with-combine launches)" if fused else
-         " (grouped GEMM: plan + gate/up + down launches)")
+        (" (grouped GEMM: counter clear + gate/up + down-with-combine launches" if fused else
+         " (grouped GEMM: gate/up + down launches") + \
+        ", after a tile-plan launch when there are several ranks or the tiles are direct-to-LDS)"
     roof["algorithmic_bytes"] = ab["mlp"]
     roof["algorithmic_flops"] = ab["mlp_flops"]
 
