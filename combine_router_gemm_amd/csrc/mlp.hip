@@ -991,6 +991,9 @@ void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
 #ifndef MOE_DEC_RS
 #define MOE_DEC_RS 2
 #endif
+#ifndef MOE_DEC_DN_RS
+#define MOE_DEC_DN_RS MOE_DEC_RS
+#endif
 #ifndef MOE_PRE_LDB
 #define MOE_PRE_LDB 2
 #endif
@@ -1119,7 +1122,7 @@ void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, i
   launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true>(
       gu, g1, stream);
   const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
-  launch_gemm<bf16_t, Op16, BM, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_RS, MOE_DEC_LDB, true,
+  launch_gemm<bf16_t, Op16, BM, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_DN_RS, MOE_DEC_LDB, true,
               COMBINE>(dn, g2, stream);
 }
 }  // namespace
