@@ -232,7 +232,7 @@ def cpu_baseline(cfg, inp_dev, max_tokens=None, fp8=False, min_seconds=10.0, max
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no collectives or "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no collectives or "
               f"multi-GPU path; the single-GPU figure is the per-GPU share.", file=sys.stderr)
         sys.exit(2)
 

@@ -3,8 +3,8 @@
 The routing is the GPU's own (route is checked in test_gpu_parity.py); each stage is then checked on the
 GPU's upstream output:
   F3 dispatch  every layout array bit-exact vs the oracle dispatch; E4M3 codes and block scales bit-exact
-               vs the oracle's quantisation of the GPU's send rows (all rows for configs 2 and 4, a sample
-               of 2048 rows plus the first and last for configs 3 and 5)
+               vs the oracle's quantisation of the GPU's send rows (all rows for the Mixtral and Kimi-share
+               decode batches, a sample of 2048 rows plus the first and last for the two prefill batches)
   F4 MLP       per-row normwise rel <= 2e-2 vs the oracle MLP on the GPU's decoded codes
   F6 layer     per-token normwise rel <= 2e-2 vs the oracle layer with fp8 dispatch (GPU ids); all-dropped
                tokens exactly 0

@@ -9,8 +9,8 @@ through the C ABI, on the GPU's own dispatch layout and expert outputs.
                                     + (k + R + 2) * 2^-24 * sum over kept slots of |w * row|,
            u the unit roundoff of the activation type: each partial adds one rounding, and both sides sum
            in fp32 (one fp32 rounding per addition; negligible for bf16, the same order as u for fp32)
-The full-size workloads are checked on every token where T <= 4096 (configs 1-4) and on 512 sampled
-tokens for config 5; the edge shapes in full.
+The full-size workloads are checked on every token where T <= 4096 (all but the 16384-token skewed
+prefill) and on 512 sampled tokens for that one; the edge shapes in full.
 """
 import numpy as np
 import pytest
