@@ -629,7 +629,17 @@ struct RegTile {
   }
   if (LDB == 1) lds_barrier();  // the next tile overwrites the LDS stage
 
-  // epilogue: lane l holds column l % S of each S x S accumulator; Op::out_row gives the rows
+  // epilogue: lane l holds column l % S of each S x S accumulator; Op::out_row gives the rows. The
+  // destination rows are loaded first, unconditionally (rows past the tile read its last row), so the
+  // loads are in flight together instead of one per store under the store's branch.
+  int orows[TM][Op::NR];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int q = 0; q < Op::NR; ++q) {
+      const int p = p0 + min(wm * WTM + i * S + Op::out_row(lane, q), m_rows - 1);
+      orows[i][q] = args.out_perm ? args.out_perm[p] : p;
+    }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -643,8 +653,7 @@ struct RegTile {
           float v;
           if (GATED) v = silu_f32(acc[i][j][q]) * acc[i][j + TN][q];
           else v = acc[i][j][q];
-          const int p = p0 + row;
-          const int orow = args.out_perm ? args.out_perm[p] : p;
+          const int orow = orows[i][q];
           if (COMBINE) st_agent(Out + (int64_t)orow * args.ldo + col, v);
           else Out[(int64_t)orow * args.ldo + col] = from_f32<T>(v);
         }
@@ -737,14 +746,17 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
   constexpr int OUT_COLS = GATED ? BN / 2 : BN;
   static_assert(NS >= 2 && NS <= 6, "2..6 LDS stages");
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE];
+  // the NS stages, then the tile's destination rows (BM ints) for the epilogue. This must stay the
+  // kernel's only LDS object: with a second one the compiler adds waits for every load in flight
+  // before LDS reads (4 more vmcnt(0) per kernel body), which cost 13 % to 2x
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * STAGE + BM * 4];
 
   const bf16_t* A = static_cast<const bf16_t*>(args.A);
   const bf16_t* W = static_cast<const bf16_t*>(args.W);
   bf16_t* __restrict__ Out = static_cast<bf16_t*>(args.Out);
   const int El = args.El;
   // the plan kernel's output (scalar loads: the plan is the same for the whole workgroup); this kernel
-  // always runs with a plan (an LDS copy measured 15 % to 2x slower here)
+  // always runs with a plan
   const int* row_start = args.plan + 2;
   const int* tile_start = args.plan + 3 + El;
   const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
@@ -910,6 +922,16 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
     constexpr int CPO = OUT_COLS / 8;  // 16-byte chunks per output row
     static_assert(BM * OUT_COLS * 2 <= NS * STAGE && CPO >= 8, "output tile must fit the stage buffers");
     auto out_off = [&](int r, int cl) { return r * OUT_COLS * 2 + (((cl >> 3) ^ (((r >> 2) & 1) << 2)) << 4) + (cl & 7) * 2; };
+    // the destination row of each tile row: one load per row, all in flight together while the
+    // accumulators go to LDS, then kept in LDS. A row-map load inside the store loop would wait for
+    // every store before it (one counter covers loads and stores) and serialise the tile's stores.
+    static_assert(BM <= NW * 64, "one row per thread");
+    int* s_orow = reinterpret_cast<int*>(smem + NS * STAGE);
+    int my_orow = 0;
+    if (tid < BM) {
+      const int p = p0 + min(tid, m_rows - 1);
+      my_orow = args.out_perm ? args.out_perm[p] : p;
+    }
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -926,6 +948,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
         }
       }
     }
+    if (tid < BM) s_orow[tid] = my_orow;
     lds_barrier();
     // with the fused combine, Out (below 2 GiB here, like every operand of this kernel) is stored at agent scope
     const __amdgpu_buffer_rsrc_t out_rsrc =
@@ -934,8 +957,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
       const int row = idx / CPO, ch = idx % CPO;
       const int col = n0 + ch * 8;
       if (row < m_rows && col < args.N) {
-        const int p = p0 + row;
-        const int orow = args.out_perm ? args.out_perm[p] : p;
+        const int orow = s_orow[row];
         if (COMBINE) st16_agent(out_rsrc, (orow * args.ldo + col) * 2, ld16(smem + out_off(row, ch * 8)));
         else st16(Out + (int64_t)orow * args.ldo + col, ld16(smem + out_off(row, ch * 8)));
       }
