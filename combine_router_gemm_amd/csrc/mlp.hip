@@ -797,7 +797,15 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
     const __amdgpu_buffer_rsrc_t b_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)l * args.w_stride), (short)0, w_bytes, 0x00020000);
 
-    // this wave's LPW load instructions per stage: byte offset (without k) and LDS offset of each
+    // this wave's LPW load instructions per stage: byte offset (without k) and LDS offset of each.
+    // The source rows of the A instructions are looked up first, unconditionally (rows past the tile
+    // read its last row), so the lookups are in flight together rather than one wait each.
+    int srcs[LPW];
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int p = p0 + min((wave * LPW + q) * RPI + lane / CPR, m_rows - 1);
+      srcs[q] = (args.a_perm && wave * LPW + q < A_INS) ? args.a_perm[p] : p;
+    }
     int voff[LPW], loff[LPW];
     bool isa[LPW];
 #pragma unroll
@@ -809,13 +817,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
         const int chunk = pos ^ dl_swz<SWZ, CPR>(r);
         isa[q] = true;
         loff[q] = ins * 1024;
-        if (r < m_rows) {
-          const int p = p0 + r;
-          const int src = args.a_perm ? args.a_perm[p] : p;
-          voff[q] = src * args.lda * 2 + chunk * 16;
-        } else {
-          voff[q] = OOB;
-        }
+        voff[q] = r < m_rows ? srcs[q] * args.lda * 2 + chunk * 16 : OOB;
       } else {
         const int r = (ins - A_INS) * RPI + r_in;
         const int chunk = pos ^ dl_swz<SWZ, CPR>(r);
