@@ -33,7 +33,9 @@ Readings taken where the pages are silent (each is listed in the design notes):
     destination ranks and El = E / R experts per rank, rank r owns experts [r*El, (r+1)*El);
   * a row routed to expert e is multiplied by local expert weights W[e mod El] (one GPU plays one rank
     and its R incoming segments are the R rank segments of its own send buffer);
-  * the expert intermediate h = silu(x Wg^T) * (x Wu^T) is stored in the activation type.
+  * the gate and up projections g = x Wg^T and u = x Wu^T are float32 values (the precision of
+    the matrix units' accumulators); h = silu(g) * u is stored in the activation type;
+  * a NaN router score ranks as -inf in the top-k selection.
 """
 from __future__ import annotations
 
@@ -72,10 +74,13 @@ def topk_select(logits, k: int) -> np.ndarray:
 
     Top-K selection over the router's scores ("Efficient and portable mixture-of-experts
     communication", section "Introductie"). Order: descending logit; equal logits are ordered by the
-    lower expert id; -0 and +0 compare equal. Written as a stable sort of the negated values, so equal
-    keys keep index order. Returns ids [T, k] int32.
+    lower expert id; -0 and +0 compare equal. The pages do not say how a NaN score ranks; here it ranks
+    as -inf (so it is chosen only when fewer than k scores are larger than -inf, and then by expert id
+    like every other tie). Written as a stable sort of the negated values, so equal keys keep index
+    order. Returns ids [T, k] int32.
     """
     lg = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    lg = np.where(np.isnan(lg), -np.inf, lg)
     order = np.argsort(-lg, axis=1, kind="stable")
     return order[:, :k].astype(np.int32)
 
@@ -210,7 +215,8 @@ def expert_mlp(rows, dt: str, row_expert, El: int, w_gate_up, w_down, F: int) ->
     """SwiGLU expert MLP on dispatched rows.
 
     Each row routed to global expert e uses local expert l = e mod El:
-        g = x Wg[l]^T,  u = x Wu[l]^T       (Wg = w_gate_up[l][:F], Wu = w_gate_up[l][F:])
+        g = x Wg[l]^T,  u = x Wu[l]^T       (Wg = w_gate_up[l][:F], Wu = w_gate_up[l][F:]),
+                                             each summed exactly (float64) and rounded to float32
         h = silu(g) * u, rounded to the activation type
         out = h Wd[l]^T, rounded to the activation type
     The expert is a small MLP run on the tokens dispatched to it ("DistributedMoE", section
@@ -231,8 +237,10 @@ def expert_mlp(rows, dt: str, row_expert, El: int, w_gate_up, w_down, F: int) ->
         xa = to_f64(rows[sel], dt)
         wgu = to_f64(np.asarray(w_gate_up[int(l)]), dt)
         wd = to_f64(np.asarray(w_down[int(l)]), dt)
-        g = xa @ wgu[:F].T
-        u = xa @ wgu[F:2 * F].T
+        # the gate and up projections are formed as float32 values (one rounding of each exact sum),
+        # then h = silu(g) * u is evaluated on them in float64 and rounded to the activation type
+        g = round_to_f32(xa @ wgu[:F].T).astype(np.float64)
+        u = round_to_f32(xa @ wgu[F:2 * F].T).astype(np.float64)
         h = to_f64(from_f64(silu(g) * u, dt), dt)
         out[sel] = h @ wd.T
     return from_f64(out, dt)

@@ -51,6 +51,20 @@ def test_scalar_closed_form_and_gate_up_order():
     assert swapped[0, 0] == np.float32(expect_sw) and swapped[0, 0] != out[0, 0]
 
 
+def test_gate_is_rounded_to_float32_before_the_activation():
+    # g = 1 + 2^-24 exactly (two products summed in float64); as a float32 value it is 1.0 (half-way,
+    # ties to even), and silu(1.0) and silu(1 + 2^-24) round to different float32 values, so the output
+    # shows which g the activation saw
+    x = np.array([[1.0, 1.0]], dtype=np.float32)
+    wgu = np.array([[1.0, 2.0 ** -24], [1.0, 0.0]], dtype=np.float32)   # gate row, then up row (u = 1)
+    wd = np.array([[1.0, 0.0]], dtype=np.float32).T.copy()               # [H=2, F=1]: out = [h, 0]
+    out = expert_mlp(x, "f32", [0], 1, [wgu], [wd], 1)
+    h_f32_gate = np.float32(1.0 / (1.0 + math.exp(-1.0)))
+    h_exact_gate = np.float32((1.0 + 2.0 ** -24) / (1.0 + math.exp(-(1.0 + 2.0 ** -24))))
+    assert h_f32_gate != h_exact_gate
+    assert out[0, 0] == h_f32_gate and out[0, 1] == 0.0
+
+
 def test_zero_down_projection_gives_zero():
     rng = np.random.default_rng(1)
     x = f64_to_bf16_bits(rng.standard_normal((5, 16)))

@@ -78,6 +78,23 @@ def test_topk_brute_force_over_every_tie_pattern(E):
             assert list(ids[i]) == _brute_topk(list(row), k), (row, k)
 
 
+def _brute_topk_nan_as_minus_inf(row, k):
+    """The same definition with a NaN score replaced by -inf before any comparison."""
+    return _brute_topk([float("-inf") if math.isnan(v) else v for v in row], k)
+
+
+@pytest.mark.parametrize("E", [1, 2, 3])
+def test_topk_brute_force_with_infinities_and_nan(E):
+    # NaN ranks as -inf; infinities order like any other value; ties (also among -inf and NaN) go to
+    # the lower expert id
+    values = [float("-inf"), -1.0, -0.0, 0.0, 1.0, float("inf"), float("nan")]
+    rows = np.array(list(itertools.product(values, repeat=E)), dtype=np.float32)
+    for k in range(1, E + 1):
+        ids = topk_select(rows, k)
+        for i, row in enumerate(rows):
+            assert list(ids[i]) == _brute_topk_nan_as_minus_inf(list(row), k), (row, k)
+
+
 def test_topk_negative_zero_equals_positive_zero():
     lg = np.array([[-0.0, 0.0, -1.0], [0.0, -0.0, -1.0]], dtype=np.float32)
     ids = topk_select(lg, 2)
