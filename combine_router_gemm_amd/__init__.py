@@ -127,12 +127,17 @@ def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, shape=None, device=No
     return t.data_ptr() if t.numel() > 0 else None
 
 
-def _stream(stream) -> Optional[int]:
+def _stream_obj(stream) -> torch.cuda.Stream:
+    """The torch stream object the call's kernels are enqueued on."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream()
     if isinstance(stream, torch.cuda.Stream):
-        return stream.cuda_stream
-    return int(stream)
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _stream(stream) -> Optional[int]:
+    return _stream_obj(stream).cuda_stream
 
 
 def _check(status: int, what: str):
@@ -204,14 +209,24 @@ class Layout:
                         p(self.expert_offset), p(self.row_token), p(self.row_slot), p(self.pair_row))
 
 
-def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device) -> Optional[torch.Tensor]:
+def _workspace(nbytes: int, workspace: Optional[torch.Tensor], device, stream) -> Optional[torch.Tensor]:
+    """The caller's workspace, or a temporary one. A temporary workspace is allocated on torch's current
+    stream and freed when the call returns, while the kernels that use it may still be queued on
+    `stream`: record_stream makes the caching allocator wait for that stream before reusing it."""
     if nbytes == 0:
         return workspace
     if workspace is None:
-        return torch.empty(nbytes, dtype=torch.uint8, device=device)
-    if workspace.numel() * workspace.element_size() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws.record_stream(_stream_obj(stream))
+        return ws
+    if _nbytes(workspace) < nbytes:
         raise MoeError(f"workspace too small: need {nbytes} bytes")
     return workspace
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    """Size in bytes of a workspace tensor of any element type."""
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 # ------------------------------------------------------------------------------------------------
@@ -232,13 +247,13 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, logit_bias: Optional[torc
         else:
             _ptr(logit_bias, "logit_bias", torch.float32, (T, E), dev)
             stride = E
-    ws = _workspace(moe_route_workspace_bytes(T, H, E, _dtype_code(x)), workspace, dev)
+    ws = _workspace(moe_route_workspace_bytes(T, H, E, _dtype_code(x)), workspace, dev, stream)
     st = load_library().moe_route(
         _ptr(x, "x", device=dev), _dtype_code(x), _ptr(w_router, "w_router", torch.float32, (E, H), dev),
         _ptr(logit_bias, "logit_bias"), stride, T, H, E, k,
         _ptr(logits, "logits", torch.float32, (T, E), dev), _ptr(topk_ids, "topk_ids", torch.int32, (T, k), dev),
         _ptr(topk_w, "topk_w", torch.float32, (T, k), dev), _ptr(ws, "workspace"),
-        0 if ws is None else ws.numel(), _stream(stream))
+        _nbytes(ws), _stream(stream))
     _check(st, "moe_route")
 
 
@@ -249,11 +264,11 @@ def moe_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, layout: Layout, send_b
     L = layout
     _ptr(x, "x", shape=(L.T, L.H), device=dev)
     _ptr(send_buf, "send_buf", x.dtype, (L.rows_max, L.H), dev)
-    ws = _workspace(moe_dispatch_workspace_bytes(L.T, L.k, L.E), workspace, dev)
+    ws = _workspace(moe_dispatch_workspace_bytes(L.T, L.k, L.E), workspace, dev, stream)
     cl = L.c_struct()
     st = load_library().moe_dispatch(
         _ptr(x, "x"), _dtype_code(x), _ptr(topk_ids, "topk_ids", torch.int32, (L.T, L.k), dev), ctypes.byref(cl),
-        _ptr(send_buf, "send_buf"), _ptr(ws, "workspace"), 0 if ws is None else ws.numel(), _stream(stream))
+        _ptr(send_buf, "send_buf"), _ptr(ws, "workspace"), _nbytes(ws), _stream(stream))
     _check(st, "moe_dispatch")
 
 
@@ -269,11 +284,11 @@ def moe_expert_mlp(send_buf: torch.Tensor, layout: Layout, w_gate_up: torch.Tens
     _ptr(w_gate_up, "w_gate_up", send_buf.dtype, (El, 2 * F, L.H), dev)
     _ptr(w_down, "w_down", send_buf.dtype, (El, L.H, F), dev)
     _ptr(out_buf, "out_buf", send_buf.dtype, (L.rows_max, L.H), dev)
-    ws = _workspace(moe_expert_mlp_workspace_bytes(L.T, L.k, L.E, L.R, L.C, F, dt), workspace, dev)
+    ws = _workspace(moe_expert_mlp_workspace_bytes(L.T, L.k, L.E, L.R, L.C, F, dt), workspace, dev, stream)
     cl = L.c_struct()
     st = load_library().moe_expert_mlp(
         _ptr(send_buf, "send_buf"), dt, ctypes.byref(cl), _ptr(w_gate_up, "w_gate_up"), _ptr(w_down, "w_down"), F,
-        _ptr(out_buf, "out_buf"), _ptr(ws, "workspace"), 0 if ws is None else ws.numel(), _stream(stream))
+        _ptr(out_buf, "out_buf"), _ptr(ws, "workspace"), _nbytes(ws), _stream(stream))
     _check(st, "moe_expert_mlp")
 
 
@@ -291,12 +306,12 @@ def moe_expert_mlp_combine(send_buf: torch.Tensor, layout: Layout, w_gate_up: to
     _ptr(w_down, "w_down", send_buf.dtype, (El, L.H, F), dev)
     _ptr(out_buf, "out_buf", send_buf.dtype, (L.rows_max, L.H), dev)
     _ptr(y, "y", send_buf.dtype, (L.T, L.H), dev)
-    ws = _workspace(moe_expert_mlp_combine_workspace_bytes(L.T, L.k, L.E, L.R, L.C, L.H, F, dt), workspace, dev)
+    ws = _workspace(moe_expert_mlp_combine_workspace_bytes(L.T, L.k, L.E, L.R, L.C, L.H, F, dt), workspace, dev, stream)
     cl = L.c_struct()
     st = load_library().moe_expert_mlp_combine(
         _ptr(send_buf, "send_buf"), dt, ctypes.byref(cl), _ptr(w_gate_up, "w_gate_up"), _ptr(w_down, "w_down"), F,
         _ptr(topk_w, "topk_w", torch.float32, (L.T, L.k), dev), _ptr(out_buf, "out_buf"), _ptr(y, "y"),
-        _ptr(ws, "workspace"), 0 if ws is None else ws.numel(), _stream(stream))
+        _ptr(ws, "workspace"), _nbytes(ws), _stream(stream))
     _check(st, "moe_expert_mlp_combine")
 
 
@@ -351,12 +366,12 @@ def moe_dispatch_fp8(x: torch.Tensor, topk_ids: torch.Tensor, layout: Layout, se
     _ptr(x, "x", torch.bfloat16, (L.T, L.H), dev)
     _ptr(send_q, "send_q", torch.uint8, (L.rows_max, L.H), dev)
     _ptr(send_scale, "send_scale", torch.float32, (L.rows_max, L.H // MOE_FP8_BLOCK), dev)
-    ws = _workspace(moe_dispatch_workspace_bytes(L.T, L.k, L.E), workspace, dev)
+    ws = _workspace(moe_dispatch_workspace_bytes(L.T, L.k, L.E), workspace, dev, stream)
     cl = L.c_struct()
     st = load_library().moe_dispatch_fp8(
         _ptr(x, "x"), MOE_BF16, _ptr(topk_ids, "topk_ids", torch.int32, (L.T, L.k), dev), ctypes.byref(cl),
         _ptr(send_q, "send_q"), _ptr(send_scale, "send_scale"), _ptr(ws, "workspace"),
-        0 if ws is None else ws.numel(), _stream(stream))
+        _nbytes(ws), _stream(stream))
     _check(st, "moe_dispatch_fp8")
 
 
@@ -373,10 +388,10 @@ def moe_expert_mlp_fp8(send_q: torch.Tensor, send_scale: torch.Tensor, layout: L
     _ptr(w_gate_up, "w_gate_up", torch.bfloat16, (El, 2 * F, L.H), dev)
     _ptr(w_down, "w_down", torch.bfloat16, (El, L.H, F), dev)
     _ptr(out_buf, "out_buf", torch.bfloat16, (L.rows_max, L.H), dev)
-    ws = _workspace(moe_expert_mlp_workspace_bytes(L.T, L.k, L.E, L.R, L.C, F, MOE_BF16), workspace, dev)
+    ws = _workspace(moe_expert_mlp_workspace_bytes(L.T, L.k, L.E, L.R, L.C, F, MOE_BF16), workspace, dev, stream)
     cl = L.c_struct()
     st = load_library().moe_expert_mlp_fp8(
         _ptr(send_q, "send_q"), _ptr(send_scale, "send_scale"), ctypes.byref(cl), _ptr(w_gate_up, "w_gate_up"),
-        _ptr(w_down, "w_down"), F, _ptr(out_buf, "out_buf"), _ptr(ws, "workspace"), 0 if ws is None else ws.numel(),
+        _ptr(w_down, "w_down"), F, _ptr(out_buf, "out_buf"), _ptr(ws, "workspace"), _nbytes(ws),
         _stream(stream))
     _check(st, "moe_expert_mlp_fp8")

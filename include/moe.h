@@ -116,11 +116,13 @@ int64_t moe_rows_max(int T, int k, int E, int C);
  *                workgroup per token; otherwise on MFMA (bf16 x: bf16 MFMA with w_router split exactly
  *                into three bf16 parts; fp32 x: fp32 MFMA)
  *   topk_ids     [T, k] int32 output: the k largest logits, descending, equal logits ordered by the
- *                lower expert id, -0 == +0 (slot 0 = best)
- *   topk_w       [T, k] fp32 output: softmax over the k selected logits (sums to 1)
+ *                lower expert id, -0 == +0 (slot 0 = best); a NaN logit ranks as -inf (ties among
+ *                infinities and NaN also go to the lower id)
+ *   topk_w       [T, k] fp32 output: softmax over the k selected logits (sums to 1); unspecified for a
+ *                token whose selected logits are not all finite
  *   workspace    device scratch of at least moe_route_workspace_bytes(T, H, E, xdt) bytes
  * Requires 1 <= k <= min(E, MOE_MAX_TOPK), E <= MOE_MAX_EXPERTS, H % 8 == 0, T >= 0 (T == 0 is a
- * no-op). NaN/Inf logits give unspecified ids.
+ * no-op).
  */
 int moe_route(const void* x, moe_dtype_t xdt, const float* w_router, const float* logit_bias,
               int64_t bias_row_stride, int T, int H, int E, int k, float* logits, int32_t* topk_ids,

@@ -20,7 +20,7 @@ import torch
 import moe_workloads as W
 import oracle
 from oracle import fp8
-from tests._hip_runner import LazyExperts, rowwise_rel_err, run_layer, run_layer_fp8, to_np
+from tests._hip_runner import LazyExperts, check_close, layer_bound, rowwise_rel_err, run_layer, run_layer_fp8, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -103,9 +103,8 @@ def test_f4_expert_mlp_fp8(wl):
     ref = oracle.expert_mlp(a, "bf16", rex[rows], cfg.El, LazyExperts(inp["w_gate_up"]), LazyExperts(inp["w_down"]),
                             cfg.F)
     got = to_np(out["out_buf"][idx])
-    err = rowwise_rel_err(oracle.to_f64(got, "bf16"), oracle.to_f64(ref, "bf16"))
-    assert np.all(err <= TOL), f"max rel err {err.max():.3e} over {len(rows)} rows"
-    print(f"[gpu] {wl}: fp8 MLP rows checked {len(rows)}, max rel err {err.max():.2e}")
+    msg = check_close(oracle.to_f64(got, "bf16"), oracle.to_f64(ref, "bf16"), "bf16", f"{wl} fp8 MLP", TOL)
+    print(f"[gpu] {msg}")
 
 
 def _oracle_layer_fp8(cfg, inp, ids, C, tokens):
@@ -125,7 +124,16 @@ def _oracle_layer_fp8(cfg, inp, ids, C, tokens):
     remap = np.full(max(lay.total, 1), -1, dtype=np.int64)
     remap[used] = np.arange(len(used))
     pr_local = np.where(pr >= 0, remap[np.maximum(pr, 0)], -1)
-    return oracle.combine(out_rows, "bf16", pr_local, w)
+    return oracle.combine(out_rows, "bf16", pr_local, w), out_rows, pr_local, w
+
+
+def _check_layer(y64, ref, what):
+    """The fp8 layer against the oracle's: row tolerance, and per element the expert-MLP element bound
+    carried through the weighted sum."""
+    y_ref, rows, pr_local, w = ref
+    f = oracle.to_f64
+    return check_close(y64, f(y_ref, "bf16"), "bf16", what, TOL,
+                       bound=layer_bound(f(y_ref, "bf16"), f(rows, "bf16"), pr_local, w, "bf16"))
 
 
 @pytest.mark.parametrize("wl", WORKLOADS)
@@ -135,8 +143,7 @@ def test_f6_layer_fp8_and_distance_to_bf16(wl):
     tokens = np.arange(cfg.T) if wl in FULL else np.sort(np.random.default_rng(21).choice(cfg.T, 48, replace=False))
     ref = _oracle_layer_fp8(cfg, inp, ids, inp["C"], tokens)
     y = oracle.to_f64(to_np(out["y"])[tokens], "bf16")
-    err = rowwise_rel_err(y, oracle.to_f64(ref, "bf16"))
-    assert np.all(err <= TOL), f"max rel err {err.max():.3e}"
+    msg = _check_layer(y, ref, f"{wl} fp8 layer")
     dropped = (to_np(out["layout"].pair_row)[tokens] < 0).all(axis=1)
     assert np.all(y[dropped] == 0.0)
     # the same layer with bf16 dispatch
@@ -146,8 +153,7 @@ def test_f6_layer_fp8_and_distance_to_bf16(wl):
     live = ~dropped
     dev = rowwise_rel_err(y[live], yb[live])
     assert np.all(dev <= FP8_VS_BF16), f"fp8 vs bf16 worst token {dev.max():.3f}"
-    print(f"[gpu] {wl}: fp8 layer tokens {len(tokens)}, max rel err {err.max():.2e}; "
-          f"distance to the bf16 layer mean {dev.mean():.3f}, max {dev.max():.3f}")
+    print(f"[gpu] {msg}; distance to the bf16 layer mean {dev.mean():.3f}, max {dev.max():.3f}")
     del bf
 
 
@@ -197,9 +203,8 @@ def test_fp8_edge_cases(name, T, H, E, k, F, R, C, routing):
     if n:
         a = fp8.dequantize_rows_bf16(to_np(out["send_q"][:n]), to_np(out["send_scale"][:n]))
         ref_ob = oracle.expert_mlp(a, "bf16", rex, E // R, to_np(inp["w_gate_up"]), to_np(inp["w_down"]), F)
-        err = rowwise_rel_err(oracle.to_f64(to_np(out["out_buf"][:n]), "bf16"), oracle.to_f64(ref_ob, "bf16"))
-        assert np.all(err <= TOL), f"MLP max rel err {err.max():.3e}"
+        check_close(oracle.to_f64(to_np(out["out_buf"][:n]), "bf16"), oracle.to_f64(ref_ob, "bf16"), "bf16",
+                    "fp8 MLP", TOL)
     ids = to_np(out["ids"])
-    ref_y = _oracle_layer_fp8(cfg, inp, ids, C, np.arange(T))
-    err = rowwise_rel_err(oracle.to_f64(to_np(out["y"]), "bf16"), oracle.to_f64(ref_y, "bf16"))
-    assert np.all(err <= TOL), f"layer max rel err {err.max():.3e}"
+    _check_layer(oracle.to_f64(to_np(out["y"]), "bf16"), _oracle_layer_fp8(cfg, inp, ids, C, np.arange(T)),
+                 "fp8 layer")

@@ -144,3 +144,42 @@ def _check_topk_ties(T, E, k, bias, H, off):
     assert np.all(np.abs(to_np(wts).astype(np.float64) - ref_w) <= 1e-6 * np.abs(ref_w) + 1e-30)
     ties = int((np.sort(lg, axis=1)[:, ::-1][:, k - 1] == np.sort(lg, axis=1)[:, ::-1][:, k]).sum()) if k < E else 0
     print(f"[gpu] top-k ties T={T} E={E} k={k}: {ties} rows with a tie at the k-th place")
+
+
+# non-finite logits: a [T, E] bias of 0, NaN, +inf or -inf on one-hot router rows. A NaN logit ranks as -inf
+# and ties (also among infinities and NaN) go to the lower id, on every router kernel: fused small-E,
+# split-K with the lane-interleaved top-k, and split-K with the row-contiguous top-k
+NONFINITE_CASES = [(300, 8, 2), (257, 16, 8), (300, 40, 5), (129, 64, 8), (700, 256, 8), (50, 384, 8)]
+
+
+@pytest.mark.parametrize("T,E,k", NONFINITE_CASES, ids=[f"T{c[0]}_E{c[1]}_k{c[2]}" for c in NONFINITE_CASES])
+def test_topk_nonfinite_logits(T, E, k):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(T * 7 + E)
+    H = ((E + 7) // 8) * 8
+    xv = rng.choice(np.array([-1.0, -0.0, 0.0, 1.0], dtype=np.float32), size=(T, H)).astype(np.float32)
+    x = torch.as_tensor(xv).to(torch.bfloat16).to(dev)
+    w = torch.zeros(E, H, dtype=torch.float32)
+    w[torch.arange(E), torch.arange(E)] = 1.0
+    w = w.to(dev)
+    special = np.array([np.nan, np.inf, -np.inf], dtype=np.float32)
+    bv = np.where(rng.random((T, E)) < 0.3, rng.choice(special, size=(T, E)), 0.0).astype(np.float32)
+    bv[: T // 8] = np.nan                                   # rows with every logit NaN
+    bv[T // 8: T // 4] = np.where(rng.random((T // 4 - T // 8, E)) < 0.8, -np.inf, np.nan)
+    b = torch.as_tensor(bv, device=dev)
+    logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+    moe.moe_route(x, w, b, k, logits, ids, wts)
+    torch.cuda.synchronize()
+    lg = to_np(logits)
+    expect = xv[:, :E] + bv
+    assert np.array_equal(lg, expect, equal_nan=True)
+    got = to_np(ids)
+    assert np.array_equal(got, oracle.topk_select(lg, k))
+    # the weights are specified where every selected logit is finite
+    sel = np.take_along_axis(lg, got.astype(np.int64), axis=1)
+    fin = np.isfinite(sel).all(axis=1)
+    ref_w = oracle.routing_weights(lg[fin], got[fin])
+    assert np.all(np.abs(to_np(wts)[fin].astype(np.float64) - ref_w) <= 1e-6 * np.abs(ref_w) + 1e-30)
+    print(f"[gpu] non-finite top-k T={T} E={E} k={k}: {int((~fin).sum())} rows select a non-finite logit")
