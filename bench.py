@@ -6,11 +6,11 @@ Prints ONE JSON line: MoE-layer tokens/s (whole step), per-stage times, dispatch
 the HBM peak, the roofline of the dominant stage (the expert-MLP grouped GEMM) and the CPU oracle timed
 on a bounded sample of the same workload.
 
-The K timed steps carry HIP events around the expert-MLP call only (its average duration gives the
-roofline); route, dispatch and combine are timed in a second, instrumented pass of K steps, because every
-event record costs GPU time between kernels.
+The K timed steps carry HIP events at every step boundary (per-step times: median and p90) and around the
+expert-MLP call (its average duration gives the roofline); route, dispatch and combine are timed in a second,
+instrumented pass of K steps, because every event record costs GPU time between kernels.
 
-  python bench.py [--gpus 1] [--steps 32] [--warmup 16] [--workload mixtral8x7b-decode]
+  python bench.py [--gpus 1] [--steps 32] [--warmup 16] [--workload large-skewed-prefill]
 """
 from __future__ import annotations
 
@@ -28,7 +28,7 @@ METRIC = "MoE-layer tokens/s on 1 MI355X; dispatch+combine GB/s and % HBM peak"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 MFMA_F32_PEAK_TFLOPS = 157.3
-DEFAULT_WORKLOAD = "mixtral8x7b-decode"
+DEFAULT_WORKLOAD = "large-skewed-prefill"
 
 
 def parse():
@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default=None,
                     help="workload name, or its position (1-5) in moe_workloads.WORKLOADS "
-                         "(default: mixtral8x7b-decode)")
+                         "(default: large-skewed-prefill)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--fused-combine", action="store_true",
                     help="fuse the combine into the expert MLP's down GEMM (moe_expert_mlp_combine): the tile "
@@ -181,9 +181,15 @@ def algorithmic_bytes(cfg, C, counts, s, fp8=False, sender=False):
                 route_flops=2 * T * E * H, mlp_flops=6 * H * F * kept)
 
 
-def cpu_baseline(cfg, inp_dev, max_tokens=None, fp8=False, min_seconds=10.0, max_seconds=30.0):
-    """Time the CPU oracle (as it stands) on the first tokens of the same workload: one bounded batch, run
-    repeatedly for about min_seconds (at most max_seconds) of CPU work."""
+def cpu_baseline(cfg, inp_dev, fp8=False, min_seconds=10.0, max_seconds=30.0, max_mlp_experts=8):
+    """Time the CPU oracle (as it stands) on the same workload, stage by stage.
+
+    Route, dispatch and combine run on the whole batch, so the capacity, the drops and the rows are the
+    workload's own. The expert MLP runs on every row of a sample of local experts (at most
+    max_mlp_experts, evenly spaced; one expert's weights on the host at a time) and its time is scaled to
+    all active local experts by the mean time per sampled expert. Combine reads the dispatched rows in
+    place of expert outputs (its cost does not depend on the values). The whole sequence repeats until
+    about min_seconds of oracle work (never past max_seconds)."""
     import numpy as np
     import torch
 
@@ -202,31 +208,60 @@ def cpu_baseline(cfg, inp_dev, max_tokens=None, fp8=False, min_seconds=10.0, max
             return t.view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()
 
-    T = cfg.T if max_tokens is None else min(cfg.T, max_tokens)
+    T, E, k, R, El = cfg.T, cfg.E, cfg.k, cfg.R, cfg.El
     dt = cfg.dtype
-    x = host(inp_dev["x"][:T])
-    bias = inp_dev["bias"]
-    bias = None if bias is None else host(bias if bias.dim() == 1 else bias[:T])
+    x = host(inp_dev["x"])
+    bias = host(inp_dev["bias"])
     wr = host(inp_dev["w_router"])
-    wgu = host(inp_dev["w_gate_up"])
-    wdn = host(inp_dev["w_down"])
     C = W.capacity(cfg, T)
-    # the same bounded batch, run again until at least min_seconds of oracle work (never past max_seconds)
-    runs, sec = 0, 0.0
-    while runs == 0 or (sec < min_seconds and sec * (runs + 1) / runs <= max_seconds):
+    stages = {"route": 0.0, "dispatch": 0.0, "expert_mlp": 0.0, "combine": 0.0}
+    runs, total = 0, 0.0
+    while runs == 0 or (total < min_seconds and total * (runs + 1) / runs <= max_seconds):
         t0 = time.perf_counter()
+        logits = oracle.router_logits(x, dt, wr, bias)
+        ids, w = oracle.topk_softmax(logits, k)
+        t1 = time.perf_counter()
         if fp8:
-            res = oracle.fp8.moe_layer_fp8(x, wr, bias, cfg.k, C, cfg.R, wgu, wdn, cfg.F)
+            lay, codes, scales = oracle.fp8.dispatch_fp8(x, ids, E, C, R)
         else:
-            res = oracle.moe_layer(x, dt, wr, bias, cfg.k, C, cfg.R, wgu, wdn, cfg.F)
-        sec += time.perf_counter() - t0
+            lay, sb = oracle.dispatch(x, dt, ids, E, C, R)
+        t2 = time.perf_counter()
+        rex = oracle.row_experts(lay.expert_offset, E)
+        local = rex % El
+        active = np.unique(local)
+        picks = active[np.unique(np.linspace(0, len(active) - 1, min(max_mlp_experts, len(active))).round().astype(int))] \
+            if len(active) else active
+        mlp_s, mlp_rows = 0.0, 0
+        for l in picks:
+            rows = np.nonzero(local == l)[0]
+            wgu = {int(l): host(inp_dev["w_gate_up"][int(l)])}
+            wdn = {int(l): host(inp_dev["w_down"][int(l)])}
+            a = oracle.fp8.dequantize_rows_bf16(codes[rows], scales[rows]) if fp8 else sb[rows]
+            tm = time.perf_counter()
+            oracle.expert_mlp(a, dt, rex[rows], El, wgu, wdn, cfg.F)
+            mlp_s += time.perf_counter() - tm
+            mlp_rows += len(rows)
+            del wgu, wdn
+        mlp_est = mlp_s * len(active) / max(len(picks), 1)
+        t3 = time.perf_counter()
+        stand_in = oracle.fp8.dequantize_rows_bf16(codes, scales) if fp8 else sb
+        oracle.combine(stand_in, dt, lay.pair_row, w)
+        t4 = time.perf_counter()
+        stages["route"] += t1 - t0
+        stages["dispatch"] += t2 - t1
+        stages["expert_mlp"] += mlp_est
+        stages["combine"] += t4 - t3
+        total += (t1 - t0) + (t2 - t1) + mlp_est + (t4 - t3)
         runs += 1
     what = " with fp8 dispatch" if fp8 else ""
-    batch = (f"the whole {cfg.name} batch ({T} tokens)" if T == cfg.T else
-             f"the first {T} of {cfg.T} tokens of {cfg.name} as one batch (capacity {C})")
-    sample = f"{batch}, {runs} oracle run{'s' if runs > 1 else ''}{what}, {sec:.1f} s in total"
-    return dict(value=T * runs / sec, unit="tokens/s", cores=int(threads), kind="oracle", sample=sample,
-                seconds=round(sec, 3), runs=runs, rows=int(res["layout"].total))
+    sample = (f"the whole {cfg.name} batch ({T} tokens, capacity {C}, {lay.total} kept rows){what}: route, dispatch "
+              f"and combine on every token; the expert MLP on all {mlp_rows} rows of {len(picks)} of the "
+              f"{len(active)} active local experts (evenly spaced), scaled by the mean time per expert; "
+              f"{runs} run{'s' if runs > 1 else ''}")
+    return dict(value=T * runs / total, unit="tokens/s", cores=int(threads), kind="oracle", sample=sample,
+                seconds_per_layer=round(total / runs, 3),
+                stages_s={n: round(v / runs, 3) for n, v in stages.items()}, runs=runs,
+                mlp_sample={"experts": int(len(picks)), "rows": int(mlp_rows), "active_local_experts": int(len(active))})
 
 
 def main():
@@ -330,14 +365,25 @@ def main():
     # expert MLP) is bracketed by events here (each event record costs a few microseconds of GPU time
     # between kernels); the other stages are timed in a separate instrumented pass below.
     mlp_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    step_events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        step_events[i].record(stream)
         step(mlp_ev=mlp_events[i])
+    step_events[args.steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     mlp_us_timed = 1e3 * sum(ev[0].elapsed_time(ev[1]) for ev in mlp_events) / args.steps
     ms_per_step = 1e3 * wall / args.steps
+    step_ms = sorted(step_events[i].elapsed_time(step_events[i + 1]) for i in range(args.steps))
+
+    def pct(q):
+        """q-quantile of the per-step times (linear interpolation)."""
+        pos = q * (len(step_ms) - 1)
+        lo = int(pos)
+        hi = min(lo + 1, len(step_ms) - 1)
+        return step_ms[lo] + (step_ms[hi] - step_ms[lo]) * (pos - lo)
 
     # instrumented pass (not part of the headline): every stage bracketed by events
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -392,6 +438,23 @@ def main():
     dc_s = (stage_us["dispatch"] + (0.0 if fused else stage_us["combine"])) * 1e-6
     dc_gbs = (ab["dispatch"] + (0 if fused else ab["combine"])) / dc_s / 1e9
     tokens_per_s = T / (ms_per_step * 1e-3)
+    # the router's roofline: its fp32 dot products run as three exact bf16 products each on the matrix
+    # cores, so its bound is the larger of its bytes at the HBM peak and 3 x its flops at the bf16 (or, for
+    # fp32 activations, 1 x at the fp32) matrix peak
+    route_s = stage_us["route"] * 1e-6
+    route_mfma_flops = ab["route_flops"] * (3 if s == 2 else 1)
+    route_bound_s = max(ab["route"] / (HBM_PEAK_GBS * 1e9), route_mfma_flops / (mfma_peak * 1e12))
+    route_roof = {"TFLOP/s": round(ab["route_flops"] / route_s / 1e12, 3),
+                  "GB/s": round(ab["route"] / route_s / 1e9, 1),
+                  "bound": "mfma" if route_mfma_flops / (mfma_peak * 1e12) >= ab["route"] / (HBM_PEAK_GBS * 1e9)
+                  else "hbm",
+                  "roofline_us": round(route_bound_s * 1e6, 2),
+                  "frac": round(route_bound_s / route_s, 4),
+                  "frac_of_fp32_peak": round(ab["route_flops"] / route_s / 1e12 / MFMA_F32_PEAK_TFLOPS, 4)}
+
+    def hbm_stage(name):
+        gbs = ab[name] / (stage_us[name] * 1e-6) / 1e9
+        return {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": ab[name]}
 
     result = {
         "metric": METRIC,
@@ -401,6 +464,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"median": round(pct(0.5), 4), "p90": round(pct(0.9), 4), "min": round(step_ms[0], 4),
+                    "max": round(step_ms[-1], 4), "source": "HIP events at every step boundary of the timed steps"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -419,8 +484,9 @@ def main():
                              "bytes": ab["dispatch"] + (0 if fused else ab["combine"]),
                              "stages": "dispatch only (the combine runs inside the expert MLP)" if fused else
                              "dispatch + combine"},
-        "route": {"TFLOP/s": round(ab["route_flops"] / (stage_us["route"] * 1e-6) / 1e12, 3),
-                  "GB/s": round(ab["route"] / (stage_us["route"] * 1e-6) / 1e9, 1)},
+        "route": route_roof,
+        "dispatch": hbm_stage("dispatch"),
+        "combine": None if fused else hbm_stage("combine"),
         "effective_assignments_per_s": round(kept / (ms_per_step * 1e-3), 1),
         "routing": {"kept_pairs": kept, "pairs": T * k, "dropped_pairs": T * k - kept,
                     "active_local_experts": active_local},
@@ -429,9 +495,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        sample_tokens = None if cfg.T <= 512 else 256
         print(f"[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, sample_tokens, fp8)
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, fp8)
     print(json.dumps(result), flush=True)
 
 
