@@ -48,6 +48,8 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
                              const float* topk_w = nullptr, void* y = nullptr, int* counter = nullptr);
 // columns per down-GEMM tile (the band of the fused combine's counters)
 int mlp_down_cols(const MlpTiles& tiles);
+// whether the variant's GEMM kernels read the plan kernel's output (then it is always launched)
+bool mlp_reads_plan(const MlpTiles& tiles);
 
 // ---- combine ----
 hipError_t launch_combine(const void* out_buf, int xdt_bf16, const moe_layout_t& L, const float* topk_w, void* y,

@@ -332,9 +332,20 @@ __device__ __forceinline__ void st_agent(float* p, float v) {
 // band, and combines it at once: y[t, band] = sum over kept slots j, ascending, of w[t, j] * out[row_j],
 // fp32, rounded once (the combine's own arithmetic, so the result equals moe_combine's bit for bit).
 // The combine of early bands thus runs while later tiles are still being computed. Nothing ever waits:
-// a workgroup either finishes a band or leaves it to the tile that will. The tile's rows were stored at
-// agent scope; every thread waits for its stores to complete before the workgroup counts them, and the
-// tile that completes a band reads the other tiles' rows at agent scope after its count returned.
+// a workgroup either finishes a band or leaves it to the tile that will.
+// Ordering between the tile that stores rows and the tile that combines them. Every access to the shared
+// rows is an agent-scope atomic access (sc1: stores write through to, and loads read from, the level that
+// is coherent across the XCDs' L2 caches), and the counters are agent-scope atomic adds. In the gfx942 /
+// gfx950 code sequences of the LLVM AMDGPU memory model, an agent-scope release is "buffer_wbl2 sc1;
+// s_waitcnt vmcnt(0)" before the releasing operation and an acquire is "s_waitcnt vmcnt(0); buffer_inv sc1"
+// after the acquiring one. The cache writeback and invalidate exist for non-atomic accesses, which may sit
+// in a non-coherent L2; accesses made with sc1 never do, so for these rows the release reduces to its wait
+// and the acquire to issuing the later loads after the acquiring operation has returned. Both are here:
+// every thread waits (vmcnt(0)) until its row stores are complete before the workgroup barrier that
+// precedes the counter adds, and the combining tile issues its sc1 row loads only after the add that
+// returned the last count (its result decides, through LDS and a barrier, which tokens are combined).
+// The L2 writeback and invalidate of a full release / acquire per tile cost more than twice the down
+// GEMM's time when they were tried (they discard the operands the other workgroups are reusing).
 // LDS: s_list holds at least BM + 1 ints and is free on entry.
 template <typename T, int NTH, int OUT_COLS>
 __device__ __forceinline__ void tile_arrive_combine(const GemmArgs& a, int p0, int m_rows, int n0, int nt,
@@ -858,6 +869,10 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
         for (int q = 0; q < Op::NR; ++q) acc[i][j][q] = 0.f;
 
     const int fr = lane & 31, fq = lane >> 5;
+    // 32-row blocks of this wave's rows that hold tile rows: the blocks past the tile's last row are
+    // neither read from LDS nor multiplied (wave-uniform), so a ragged tile of an expert's last rows
+    // costs matrix time only for its real blocks
+    const int mb = min(TM, max(0, (m_rows - wm * WTM + S - 1) / S));
     // fragments of K step kk + 1 are requested before the MFMAs of step kk are issued (two fragment
     // buffers), so LDS latency overlaps the matrix work of the same wave
     auto load_frags = [&](const unsigned char* base, int kk, u32x4 (&af)[TM][1], u32x4 (&bfg)[NACC][1]) {
@@ -865,7 +880,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * WTM + i * S + fr;
-        af[i][0] = ld16(base + r * ROWB + ((c ^ dl_swz<SWZ, CPR>(r)) << 4));
+        if (i < mb) af[i][0] = ld16(base + r * ROWB + ((c ^ dl_swz<SWZ, CPR>(r)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < NACC; ++j) {
@@ -893,8 +908,10 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
         if (ks + 1 < KSTEPS) load_frags(base, (ks + 1) * Op::KS, af[(ks + 1) & 1], bfg[(ks + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
+          if (i < mb) {
 #pragma unroll
-          for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[ks & 1][i], bfg[ks & 1][j]);
+            for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[ks & 1][i], bfg[ks & 1][j]);
+          }
       }
     };
 
@@ -920,10 +937,13 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
     // epilogue through LDS, free once every wave is past the last stage: the waves write their bf16
     // results (lane l holds column l % 32, rows 8*(q/4) + 4*(l/32) + q%4 of each 32x32 block), then
     // every lane stores whole 16-byte row chunks. Chunk c of tile row r sits at c ^ (4 * ((r >> 2) & 1)),
-    // which puts rows r and r + 4 (written by one instruction) on different LDS banks.
-    constexpr int CPO = OUT_COLS / 8;  // 16-byte chunks per output row
-    static_assert(BM * OUT_COLS * 2 <= NS * STAGE && CPO >= 8, "output tile must fit the stage buffers");
-    auto out_off = [&](int r, int cl) { return r * OUT_COLS * 2 + (((cl >> 3) ^ (((r >> 2) & 1) << 2)) << 4) + (cl & 7) * 2; };
+    // which puts rows r and r + 4 (written by one instruction) on different LDS banks. An output tile
+    // larger than the stage buffers goes out in OCH column parts, each written by the waves owning it.
+    constexpr int OCH = (BM * OUT_COLS * 2 <= NS * STAGE) ? 1 : 2;
+    constexpr int OCW = OUT_COLS / OCH;  // columns per part
+    constexpr int CPO = OCW / 8;         // 16-byte chunks per output row of a part
+    static_assert(WN % OCH == 0 && BM * OCW * 2 <= NS * STAGE && CPO >= 8, "output parts must fit the stage buffers");
+    auto out_off = [&](int r, int cl) { return r * OCW * 2 + (((cl >> 3) ^ (((r >> 2) & 1) << 2)) << 4) + (cl & 7) * 2; };
     // the destination row of each tile row: one load per row, all in flight together while the
     // accumulators go to LDS, then kept in LDS. A row-map load inside the store loop would wait for
     // every store before it (one counter covers loads and stores) and serialise the tile's stores.
@@ -934,25 +954,304 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
       const int p = p0 + min(tid, m_rows - 1);
       my_orow = args.out_perm ? args.out_perm[p] : p;
     }
+    // with the fused combine, Out (below 2 GiB here, like every operand of this kernel) is stored at agent scope
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Out, (short)0, COMBINE ? args.out_bytes : 0, 0x00020000);
+#pragma unroll
+    for (int oc = 0; oc < OCH; ++oc) {
+      lds_barrier();  // the stages (or the previous part) are no longer read
+      if (wn / (WN / OCH) == oc) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int cl = (GATED ? wn * (BN / 2 / WN) + j * S + fr : wn * (BN / WN) + j * S + fr) - oc * OCW;
+#pragma unroll
+            for (int q = 0; q < Op::NR; ++q) {
+              const int row = wm * WTM + i * S + Op::out_row(lane, q);
+              float v;
+              if (GATED) v = silu_f32(acc[i][j][q]) * acc[i][j + TN][q];
+              else v = acc[i][j][q];
+              *reinterpret_cast<bf16_t*>(smem + out_off(row, cl)) = (bf16_t)v;
+            }
+          }
+        }
+      }
+      if (oc == 0 && tid < BM) s_orow[tid] = my_orow;
+      lds_barrier();
+      for (int idx = tid; idx < BM * CPO; idx += NW * 64) {
+        const int row = idx / CPO, ch = idx % CPO;
+        const int col = n0 + oc * OCW + ch * 8;
+        if (row < m_rows && col < args.N) {
+          const int orow = s_orow[row];
+          if (COMBINE) st16_agent(out_rsrc, (orow * args.ldo + col) * 2, ld16(smem + out_off(row, ch * 8)));
+          else st16(Out + (int64_t)orow * args.ldo + col, ld16(smem + out_off(row, ch * 8)));
+        }
+      }
+    }
+    if (COMBINE) {
+      lds_barrier();  // every wave has read its output chunks before the token list overwrites them
+      tile_arrive_combine<bf16_t, NW * 64, OUT_COLS>(args, p0, m_rows, n0, nt, n_tiles, reinterpret_cast<int*>(smem));
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Compute-bound bf16 GEMM, direct global -> LDS loads, ping-pong wave schedule
+// ------------------------------------------------------------------------------------------------
+// Eight waves, two per SIMD (wave w runs on SIMD w % 4), each owning a 64 x 128 block of the tile (2 x 4
+// MFMA 32x32x16 accumulators). The waves form two groups, 0..3 and 4..7, one wave of each on every SIMD.
+// The K loop is cut into phases separated by workgroup barriers; in every phase one group reads a whole
+// 64-deep stage of fragments from LDS into registers (its memory phase) while the other group issues the
+// 32 MFMAs of the stage it read in the phase before (its compute phase), so each SIMD's matrix unit
+// always has a wave feeding it and the barrier and LDS latency fall in the memory phases:
+//   phase 2s:     group 0 reads stage s      group 1 computes stage s - 1
+//   phase 2s + 1: group 0 computes stage s   group 1 reads stage s
+// Two LDS stage buffers. Stage s + 1 is loaded into the buffer stage s - 1 left, by every wave, in phase
+// 2s (group 1 interleaves its loads with its MFMAs), and waited for at the end of phase 2s + 1. Stages 0
+// and 1 are loaded before phase 0. Every wave passes the same 2 nk + 1 barriers per tile.
+// Chunks are XOR-swizzled in LDS as in the other direct-to-LDS kernel (chunk c of row r at c ^ ((r >> 1)
+// & 7)), so the 32-row fragment reads hit distinct banks. Requires K % 64 == 0 and operand buffers below
+// 2 GiB.
+#ifndef MOE_PP_KPH
+#define MOE_PP_KPH 2
+#endif
+// calls f(std::integral_constant<int, i>) for i = 0 .. N - 1 (compile-time loop index)
+template <int N, int I = 0, typename Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+template <int BM, int BN, int WM, int WN, bool GATED, bool COMBINE = false>
+__global__ __launch_bounds__(512) void mlp_gemm_pp_kernel(GemmArgs args, int a_bytes) {
+  static_assert(!COMBINE || !GATED, "the combine follows the down GEMM");
+  using Op = Op32;
+  constexpr int NW = 8, BK = 64, S = 32, ROWB = BK * 2, CPR = 8, RPI = 8;
+  static_assert(WM * WN == NW, "eight waves");
+  constexpr int A_INS = BM / RPI, B_INS = BN / RPI;  // 1 KB wave loads per stage
+  static_assert((A_INS + B_INS) % NW == 0, "wave loads must split evenly");
+  constexpr int LPW = (A_INS + B_INS) / NW;
+  constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int WTM = BM / WM, TM = WTM / S;
+  constexpr int TN = GATED ? (BN / 2 / WN) / S : (BN / WN) / S;
+  constexpr int NACC = GATED ? 2 * TN : TN;
+  constexpr int OUT_COLS = GATED ? BN / 2 : BN;
+  constexpr int KSTEPS = BK / Op::KS;
+  constexpr int KPH = MOE_PP_KPH, UPS = KSTEPS / KPH;  // K steps per phase, phases per stage and group
+  static_assert(KSTEPS % KPH == 0, "phases split a stage evenly");
+  constexpr int OUT_BYTES = BM * OUT_COLS * 2;
+  constexpr int SMEM = (2 * STAGE > OUT_BYTES + BM * 4 ? 2 * STAGE : OUT_BYTES + BM * 4);
+  static_assert(TM >= 1 && TN >= 1, "wave tile too small");
+  static_assert(SMEM <= 160 * 1024, "LDS");
+  // the two stage buffers; after the last stage the output tile and its destination rows reuse them
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+
+  const bf16_t* A = static_cast<const bf16_t*>(args.A);
+  const bf16_t* W = static_cast<const bf16_t*>(args.W);
+  bf16_t* __restrict__ Out = static_cast<bf16_t*>(args.Out);
+  const int El = args.El;
+  const int* row_start = args.plan + 2;
+  const int* tile_start = args.plan + 3 + El;
+  const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
+  const int total = args.plan[0] * n_tiles;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int wm = wave / WN, wn = wave % WN;
+  const int nk = args.K / BK;
+  const int OOB = 0x7ffffff0;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, a_bytes, 0x00020000);
+  const int w_bytes = (int)(args.w_stride * 2);
+
+  const int G = gridDim.x;
+  int t_begin = blockIdx.x, t_end = total, t_step = G;
+  if ((G & 7) == 0 && G >= 8) {
+    const int x = blockIdx.x & 7, per = (total + 7) >> 3;
+    t_begin = x * per + (blockIdx.x >> 3);
+    t_end = min(total, (x + 1) * per);
+    t_step = G >> 3;
+  }
+
+  const int fr = lane & 31, fq = lane >> 5;
+  for (int tile = t_begin; tile < t_end; tile += t_step) {
+    int lo = 0, hi = El;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_start[mid] * n_tiles <= tile) lo = mid;
+      else hi = mid;
+    }
+    const int l = lo;
+    const int mt_l = tile_start[l + 1] - tile_start[l];
+    const int local = tile - tile_start[l] * n_tiles;
+    const int nt = local / mt_l, mt = local % mt_l;
+    const int p0 = row_start[l] + mt * BM;
+    const int m_rows = min(BM, row_start[l + 1] - p0);
+    const int n0 = nt * OUT_COLS;
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)l * args.w_stride), (short)0, w_bytes, 0x00020000);
+
+    // this wave's LPW load instructions per stage (instruction wave * LPW + q of the stage's A_INS + B_INS):
+    // byte offset without k, and whether it loads A. The A rows are looked up together first.
+    int srcs[LPW];
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int p = p0 + min((wave * LPW + q) * RPI + lane / CPR, m_rows - 1);
+      srcs[q] = (args.a_perm && wave * LPW + q < A_INS) ? args.a_perm[p] : p;
+    }
+    int voff[LPW];
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int ins = wave * LPW + q;
+      const int r_in = lane / CPR, pos = lane % CPR;
+      if (ins < A_INS) {
+        const int r = ins * RPI + r_in;
+        const int chunk = pos ^ dl_swz<1, CPR>(r);
+        voff[q] = r < m_rows ? srcs[q] * args.lda * 2 + chunk * 16 : OOB;
+      } else {
+        const int r = (ins - A_INS) * RPI + r_in;
+        const int chunk = pos ^ dl_swz<1, CPR>(r);
+        int wrow, ncol;
+        if (GATED) {
+          const int half = r / (BN / 2), rr = r % (BN / 2);
+          ncol = n0 + rr;
+          wrow = ncol + half * args.up_offset;
+        } else {
+          ncol = n0 + r;
+          wrow = ncol;
+        }
+        voff[q] = ncol < args.N ? wrow * args.K * 2 + chunk * 16 : OOB;
+      }
+    }
+    auto issue = [&](int st) {
+      const int kb = st * BK * 2;
+      unsigned char* base = smem + (st & 1) * STAGE;
+#pragma unroll
+      for (int q = 0; q < LPW; ++q) {
+        const int ins = wave * LPW + q;  // wave-uniform: A or B, and the LDS offset, are scalar
+        const int vo = voff[q] == OOB ? OOB : voff[q] + kb;
+        if (ins < A_INS) {
+          auto* dst = (__attribute__((address_space(3))) void*)(base + ins * 1024);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, vo, 0, 0, 0);
+        } else {
+          auto* dst = (__attribute__((address_space(3))) void*)(base + A_BYTES + (ins - A_INS) * 1024);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dst, 16, vo, 0, 0, 0);
+        }
+      }
+    };
+
+    typename Op::Acc acc[TM][NACC];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < NACC; ++j)
+#pragma unroll
+        for (int q = 0; q < Op::NR; ++q) acc[i][j][q] = 0.f;
+
+    // one phase's fragments (KPH K steps of a stage): [K step][A blocks, then B blocks]
+    u32x4 frag[KPH][TM + NACC];
+    // K steps ks0 .. ks0 + KPH - 1 of the stage in buffer `slot`. Every fragment row r = (32-aligned block
+    // base) + fr, so its chunk swizzle (r >> 1) & 7 is (fr >> 1) & 7 for every block.
+    auto read_unit = [&](int slot, auto ks0_c) {
+      constexpr int ks0 = decltype(ks0_c)::value;
+      const unsigned char* base = smem + slot * STAGE + fr * ROWB;
+      const int sw = (fr >> 1) & 7;
+#pragma unroll
+      for (int ks = 0; ks < KPH; ++ks) {
+        const int xo = ((((ks0 + ks) * 2 + fq) ^ sw) << 4);  // this lane's 16-byte chunk of the K step
+#pragma unroll
+        for (int i = 0; i < TM; ++i) frag[ks][i] = ld16(base + (wm * WTM + i * S) * ROWB + xo);
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) {
+          int r0;
+          if (GATED) {
+            const int half = j / TN, jj = j % TN;
+            r0 = half * (BN / 2) + wn * (BN / 2 / WN) + jj * S;
+          } else {
+            r0 = wn * (BN / WN) + j * S;
+          }
+          frag[ks][TM + j] = ld16(base + A_BYTES + r0 * ROWB + xo);
+        }
+      }
+    };
+    auto compute_unit = [&]() {
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < KPH; ++ks)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < NACC; ++j) {
+            const u32x4 a1[1] = {frag[ks][i]};
+            const u32x4 b1[1] = {frag[ks][TM + j]};
+            Op::step(acc[i][j], a1, b1);
+          }
+      __builtin_amdgcn_s_setprio(0);
+    };
+    auto phase_end = [&](bool wait_loads) {
+      if (wait_loads) wait_vmcnt<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // the previous tile's output stores are done and every wave is past its LDS reads
+    wait_vmcnt<0>();
     lds_barrier();
+    issue(0);
+    if (nk > 1) issue(1);
+    if (nk > 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    // Every wave runs the same sequence: read unit u, barrier, compute unit u, barrier. Group 1 passes one
+    // barrier first, so it runs one phase behind group 0, and group 0 passes one at the end.
+    if (grp == 1) phase_end(false);
+    for (int st = 0; st < nk; ++st) {
+      const int slot = st & 1;
+      static_for<UPS>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        // stage st + 1 goes into the buffer stage st - 1 left: group 0 is at global phase 2 UPS st, group 1 at
+        // the phase after, and both groups finished reading stage st - 1 at global phase 2 UPS st - 1
+        if (j == 0 && st >= 1 && st + 1 < nk) issue(st + 1);
+        read_unit(slot, std::integral_constant<int, j * KPH>{});
+        // stage st + 1 must have landed by the end of global phase 2 UPS (st + 1) - 1: that is the end of
+        // this read phase for group 1 and of the compute phase below for group 0
+        phase_end(j == UPS - 1 && grp == 1);
+        compute_unit();
+        phase_end(j == UPS - 1 && grp == 0);
+      });
+    }
+    if (grp == 0) phase_end(false);
+
+    // epilogue through LDS (both stage buffers are free): the waves write their bf16 results, then every
+    // lane stores whole 16-byte row chunks. Chunk c of tile row r sits at c ^ (4 * ((r >> 2) & 1)).
+    constexpr int CPO = OUT_COLS / 8;
+    static_assert(CPO >= 8, "output rows of at least 64 columns");
+    auto out_off = [&](int r, int cl) { return r * OUT_COLS * 2 + (((cl >> 3) ^ (((r >> 2) & 1) << 2)) << 4) + (cl & 7) * 2; };
+    int* s_orow = reinterpret_cast<int*>(smem + OUT_BYTES);
+    int my_orow = 0;
+    if (tid < BM) {
+      const int pp = p0 + min(tid, m_rows - 1);
+      my_orow = args.out_perm ? args.out_perm[pp] : pp;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int cl = GATED ? wn * (BN / 2 / WN) + j * S + fr : wn * (BN / WN) + j * S + fr;
 #pragma unroll
-        for (int q = 0; q < Op::NR; ++q) {
-          const int row = wm * WTM + i * S + Op::out_row(lane, q);
+        for (int qq = 0; qq < Op::NR; ++qq) {
+          const int row = wm * WTM + i * S + Op::out_row(lane, qq);
           float v;
-          if (GATED) v = silu_f32(acc[i][j][q]) * acc[i][j + TN][q];
-          else v = acc[i][j][q];
+          if (GATED) v = silu_f32(acc[i][j][qq]) * acc[i][j + TN][qq];
+          else v = acc[i][j][qq];
           *reinterpret_cast<bf16_t*>(smem + out_off(row, cl)) = (bf16_t)v;
         }
       }
     }
     if (tid < BM) s_orow[tid] = my_orow;
     lds_barrier();
-    // with the fused combine, Out (below 2 GiB here, like every operand of this kernel) is stored at agent scope
     const __amdgpu_buffer_rsrc_t out_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)Out, (short)0, COMBINE ? args.out_bytes : 0, 0x00020000);
     for (int idx = tid; idx < BM * CPO; idx += NW * 64) {
@@ -1125,6 +1424,18 @@ bool dl_fits(int64_t rows_max, int H, int F) {
          wgu_bytes < lim && wdn_bytes < lim;
 }
 
+#ifndef MOE_PP
+#define MOE_PP 1
+#endif
+template <int BM, int BN, int WM, int WN, bool COMBINE>
+void launch_pp(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
+               int64_t h_bytes, int num_cus, hipStream_t stream) {
+  const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, BN / 2), num_cus, 1);
+  mlp_gemm_pp_kernel<BM, BN, WM, WN, true><<<g1, 512, 0, stream>>>(gu, (int)send_bytes);
+  const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, BN), num_cus, 1);
+  mlp_gemm_pp_kernel<BM, BN, WM, WN, false, COMBINE><<<g2, 512, 0, stream>>>(dn, (int)h_bytes);
+}
+
 template <int BM, int BN, int WM, int WN, int NS, bool SPREAD, bool COMBINE>
 void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
                int64_t h_bytes, int num_cus, hipStream_t stream) {
@@ -1160,13 +1471,19 @@ MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16) {
   if (per_expert < 128) return per_expert >= MOE_DEC_TALL_MIN_ROWS ? MlpTiles{64, 5} : MlpTiles{32, 1};
   if (!dl_fits(rows_max, H, F)) return MlpTiles{MOE_PRE_BM, 0};
   if (per_expert >= MOE_DL_TALL_MIN_ROWS) return MlpTiles{256, 4};
+  if (per_expert >= 256) return MlpTiles{320, 6};
   return MlpTiles{128, 3};
 }
+
+// the direct-to-LDS kernels (variants 3, 4 and 6) always read the plan kernel's output; the
+// register-staged ones build it themselves when there is one rank
+bool mlp_reads_plan(const MlpTiles& tiles) { return tiles.variant == 3 || tiles.variant == 4 || tiles.variant == 6; }
 
 int mlp_down_cols(const MlpTiles& tiles) {
   switch (tiles.variant) {
     case 3: return MOE_DL_BN;
     case 4: return MOE_DLT_BN;
+    case 6: return 256;
     case 0: return MOE_PRE_BN;
     case 1:
     case 5: return MOE_DEC_DN_BN;
@@ -1180,12 +1497,24 @@ void launch_gemms(const GemmArgs& gu, const GemmArgs& dn, const MlpTiles& tiles,
                   int H, int F, int num_cus, hipStream_t stream) {
   switch (tiles.variant) {
     case 3:
-      launch_dl<128, MOE_DL_BN, MOE_DL_WM, MOE_DL_WN, MOE_DL_NS, MOE_DL_SPREAD, COMBINE>(
-          gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
+      if (MOE_PP)
+        launch_pp<128, 512, 2, 4, COMBINE>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
+                                           rows_max * (int64_t)F * 2, num_cus, stream);
+      else
+        launch_dl<128, MOE_DL_BN, MOE_DL_WM, MOE_DL_WN, MOE_DL_NS, MOE_DL_SPREAD, COMBINE>(
+            gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
       break;
     case 4:
-      launch_dl<256, MOE_DLT_BN, MOE_DLT_WM, MOE_DLT_WN, MOE_DLT_NS, MOE_DLT_SPREAD, COMBINE>(
-          gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
+      if (MOE_PP)
+        launch_pp<256, 256, 4, 2, COMBINE>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
+                                           rows_max * (int64_t)F * 2, num_cus, stream);
+      else
+        launch_dl<256, MOE_DLT_BN, MOE_DLT_WM, MOE_DLT_WN, MOE_DLT_NS, MOE_DLT_SPREAD, COMBINE>(
+            gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
+      break;
+    case 6:  // one 320-row tile holds a whole expert of up to 320 rows: its weights are read once
+      launch_dl<320, 256, 2, 4, 2, false, COMBINE>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
+                                                   rows_max * (int64_t)F * 2, num_cus, stream);
       break;
     case 0: {  // bf16, many rows per expert, operands staged through registers
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_PRE_BN / 2), num_cus, MOE_PRE_WPC);
@@ -1234,7 +1563,7 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   // with one rank the send rows are already grouped by local expert: the register-staged GEMMs build the
   // plan's starts from the expert offsets themselves and read rows in send order, with no plan launch
   // (the direct-to-LDS kernels always read the plan kernel's output)
-  const bool own_plan = L.R > 1 || tiles.variant == 3 || tiles.variant == 4;
+  const bool own_plan = L.R > 1 || mlp_reads_plan(tiles);
   if (own_plan) {
     const int plan_blocks = (int)(rows_max > 0 ? ceil_div_host64(rows_max, PLAN_ROWS_PER_WG) : 1);
     mlp_plan_kernel<<<plan_blocks, PLAN_THREADS, 0, stream>>>(L.expert_kept, L.expert_offset, L.E, El, tiles.BM,
@@ -1281,6 +1610,8 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   dn.w_bytes = buffer_bytes(dn.w_stride * (xdt_bf16 ? 2 : 4));
   dn.k_rotate = k_rotate_for(F, xdt_bf16 ? 2 : 4);
 
+  // the direct-to-LDS kernels dereference the plan: never launch them without one
+  if (mlp_reads_plan(tiles) && (gu.plan == nullptr || dn.plan == nullptr)) return hipErrorInvalidValue;
   if (y != nullptr) {
     // the combine fused into the down GEMM: counters zeroed and the y rows of tokens with no kept slot
     // cleared first

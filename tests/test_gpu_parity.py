@@ -262,6 +262,8 @@ EDGE = [
     # direct-to-LDS grouped GEMM: 128-row tiles (400 rows per expert), then 256-row tiles (2200 rows per
     # local expert); F = 192 and H = 192 / 320 leave a ragged last column tile in both GEMMs
     ("dl128_ragged", 900, 192, 4, 2, 192, 1, 400, "bf16", "zipf"),
+    # 128-row direct-to-LDS tiles (capacity 200 rows per expert), ragged
+    ("dl128_cap200", 700, 128, 8, 2, 128, 2, 200, "bf16", "zipf"),
     ("dl256_ragged_R2", 2600, 320, 4, 2, 192, 2, 1100, "bf16", "zipf"),
     # 64-row weight-streaming tiles (capacity 75 rows per expert on average), hot experts over 64 rows
     ("dec64_multi_mtile", 300, 128, 8, 2, 96, 1, 100, "bf16", "zipf"),
