@@ -19,13 +19,15 @@ import torch
 
 __all__ = ["MOE_F32", "MOE_BF16", "MOE_FP8_BLOCK", "MoeError", "Layout", "library_path", "load_library",
            "moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_dispatch_fp8", "moe_expert_mlp_fp8",
-           "moe_combine_send", "moe_combine_recv", "moe_expert_mlp_combine",
+           "moe_combine_send", "moe_combine_recv", "moe_expert_mlp_combine", "moe_dispatch_noalloc",
+           "MOE_DISPATCH_NOALLOC_MAX_WORKSPACE",
            "moe_expert_mlp_combine_workspace_bytes", "moe_rows_max", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
            "moe_expert_mlp_workspace_bytes", "moe_status_string", "EXPORTED_SYMBOLS"]
 
 MOE_F32 = 0
 MOE_BF16 = 1
 MOE_FP8_BLOCK = 128  # hidden elements per fp8 block scale
+MOE_DISPATCH_NOALLOC_MAX_WORKSPACE = 4 << 20  # bytes of moe_dispatch_noalloc's static scratch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libmoe_gfx950.so"
@@ -33,7 +35,8 @@ _LIB_NAME = "libmoe_gfx950.so"
 EXPORTED_SYMBOLS = ("moe_status_string", "moe_rows_max", "moe_route_workspace_bytes", "moe_route",
                     "moe_dispatch_workspace_bytes", "moe_dispatch", "moe_expert_mlp_workspace_bytes",
                     "moe_expert_mlp", "moe_combine", "moe_dispatch_fp8", "moe_expert_mlp_fp8", "moe_combine_send",
-                    "moe_combine_recv", "moe_expert_mlp_combine", "moe_expert_mlp_combine_workspace_bytes")
+                    "moe_combine_recv", "moe_expert_mlp_combine", "moe_expert_mlp_combine_workspace_bytes",
+                    "moe_dispatch_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -77,6 +80,8 @@ def load_library():
     lib.moe_dispatch_workspace_bytes.restype = sz
     lib.moe_dispatch.argtypes = [vp, i32, vp, ctypes.POINTER(_CLayout), vp, vp, sz, vp]
     lib.moe_dispatch.restype = i32
+    lib.moe_dispatch_noalloc.argtypes = [vp, i32, vp, ctypes.POINTER(_CLayout), vp, vp]
+    lib.moe_dispatch_noalloc.restype = i32
     lib.moe_expert_mlp_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.moe_expert_mlp_workspace_bytes.restype = sz
     lib.moe_expert_mlp.argtypes = [vp, i32, ctypes.POINTER(_CLayout), vp, vp, i32, vp, vp, sz, vp]
@@ -270,6 +275,21 @@ def moe_dispatch(x: torch.Tensor, topk_ids: torch.Tensor, layout: Layout, send_b
         _ptr(x, "x"), _dtype_code(x), _ptr(topk_ids, "topk_ids", torch.int32, (L.T, L.k), dev), ctypes.byref(cl),
         _ptr(send_buf, "send_buf"), _ptr(ws, "workspace"), _nbytes(ws), _stream(stream))
     _check(st, "moe_dispatch")
+
+
+def moe_dispatch_noalloc(x: torch.Tensor, topk_ids: torch.Tensor, layout: Layout, send_buf: torch.Tensor,
+                         stream=None) -> None:
+    """moe_dispatch with the library's static per-GPU scratch instead of a workspace (allocates nothing).
+    Calls that may overlap on one GPU race; calls on one stream are ordered."""
+    dev = x.device
+    L = layout
+    _ptr(x, "x", shape=(L.T, L.H), device=dev)
+    _ptr(send_buf, "send_buf", x.dtype, (L.rows_max, L.H), dev)
+    cl = L.c_struct()
+    st = load_library().moe_dispatch_noalloc(
+        _ptr(x, "x"), _dtype_code(x), _ptr(topk_ids, "topk_ids", torch.int32, (L.T, L.k), dev), ctypes.byref(cl),
+        _ptr(send_buf, "send_buf"), _stream(stream))
+    _check(st, "moe_dispatch_noalloc")
 
 
 def moe_expert_mlp(send_buf: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor, w_down: torch.Tensor,

@@ -3,10 +3,35 @@
 // the caller's stream.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace {
+
+// Scratch of moe_dispatch_noalloc: one static device array per GPU (each device that loads the library
+// holds its own copy). In host code `scratch` names a host-side stand-in, not device memory: kernels and
+// copies are only ever given the device address that hipGetSymbolAddress returns for the current device.
+__device__ __align__(256) unsigned char scratch[MOE_DISPATCH_NOALLOC_MAX_WORKSPACE];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on the first call there.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_HIP;
+  if (dev >= kScratchDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 // Compute units of the current device (cached per device id; a benign race fills the same value).
 int device_cus() {
@@ -122,6 +147,29 @@ int moe_dispatch(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const 
   int* blk_count = reinterpret_cast<int*>(ws);
   int* pair_local =
       reinterpret_cast<int*>(ws + moe::align256((size_t)moe::dispatch_num_blocks(L.T) * L.E * sizeof(int)));
+  return hip_status(moe::launch_dispatch(x, xdt == MOE_BF16, topk_ids, L, send_buf, blk_count, pair_local, stream));
+}
+
+int moe_dispatch_noalloc(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const moe_layout_t* layout,
+                         void* send_buf, hipStream_t stream) {
+  if (!valid_dtype(xdt)) return MOE_ERR_UNSUPPORTED;
+  const int st = check_layout(layout);
+  if (st != MOE_OK) return st;
+  const moe_layout_t& L = *layout;
+  const int64_t rows = moe_rows_max(L.T, L.k, L.E, L.C);
+  if (L.T > 0 && (!x || !topk_ids)) return MOE_ERR_INVALID;
+  if (rows > 0 && !send_buf) return MOE_ERR_INVALID;
+  if (!al16(x) || !al16(send_buf) || !al4(topk_ids)) return MOE_ERR_INVALID;
+  if (moe_dispatch_workspace_bytes(L.T, L.k, L.E) > MOE_DISPATCH_NOALLOC_MAX_WORKSPACE) return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const int sst = scratch_address(&ws);
+  if (sst != MOE_OK) return sst;
+  // the same carving as moe_dispatch's workspace; the kernels write every entry they later read, so
+  // the array's contents from an earlier call need no clearing
+  char* base = static_cast<char*>(ws);
+  int* blk_count = reinterpret_cast<int*>(base);
+  int* pair_local =
+      reinterpret_cast<int*>(base + moe::align256((size_t)moe::dispatch_num_blocks(L.T) * L.E * sizeof(int)));
   return hip_status(moe::launch_dispatch(x, xdt == MOE_BF16, topk_ids, L, send_buf, blk_count, pair_local, stream));
 }
 

@@ -156,6 +156,23 @@ size_t moe_dispatch_workspace_bytes(int T, int k, int E);
 int moe_dispatch(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const moe_layout_t* layout,
                  void* send_buf, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): no workspace argument.
+ * Its scratch (per-block expert counts and in-block ranks) is a static device array of
+ * MOE_DISPATCH_NOALLOC_MAX_WORKSPACE bytes inside the library, one per GPU, held until the process
+ * ends; its address is looked up once per device on the first call there. Arguments, outputs and
+ * results are those of moe_dispatch, bit for bit.
+ * Returns MOE_ERR_UNSUPPORTED (nothing enqueued) when moe_dispatch_workspace_bytes(T, k, E) exceeds
+ * MOE_DISPATCH_NOALLOC_MAX_WORKSPACE (e.g. 65536 tokens x top-8 x 512 experts still fits), and
+ * MOE_ERR_HIP if the array's address cannot be found. Every call on one GPU uses the same array:
+ * calls that may overlap on one GPU (different streams without ordering between them) race and
+ * must not be made. Calls on one stream are ordered and safe.
+ */
+#define MOE_DISPATCH_NOALLOC_MAX_WORKSPACE (4u << 20)
+int moe_dispatch_noalloc(const void* x, moe_dtype_t xdt, const int32_t* topk_ids, const moe_layout_t* layout,
+                         void* send_buf, hipStream_t stream);
+
 /* Bytes of scratch `workspace` moe_expert_mlp needs for this layout and FFN width. */
 size_t moe_expert_mlp_workspace_bytes(int T, int k, int E, int R, int C, int F, moe_dtype_t xdt);
 

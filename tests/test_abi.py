@@ -125,6 +125,22 @@ def test_dispatch_rejects_invalid_arguments(lib):
     assert call(_layout(), wsb=16) == MOE_ERR_INVALID
 
 
+def test_dispatch_noalloc_rejects_invalid_arguments_and_sizes_beyond_its_scratch(lib):
+    def call(L, xdt=moe.MOE_BF16, x=FAKE, ids=FAKE, sb=FAKE):
+        return lib.moe_dispatch_noalloc(x, xdt, ids, ctypes.byref(L), sb, None)
+    assert lib.moe_dispatch_noalloc(FAKE, moe.MOE_BF16, FAKE, None, FAKE, None) == MOE_ERR_INVALID
+    assert call(_layout(E=10, R=3)) == MOE_ERR_INVALID
+    assert call(_layout(H=60)) == MOE_ERR_UNSUPPORTED
+    assert call(_layout(), xdt=3) == MOE_ERR_UNSUPPORTED
+    assert call(_layout(), sb=None) == MOE_ERR_INVALID
+    assert call(_layout(), x=ctypes.c_void_p(0x1008)) == MOE_ERR_INVALID
+    # the static scratch holds (T / 256 blocks) x E counts and T * k ranks: 65536 x 8 x 512 fits, more does not
+    cap = moe.MOE_DISPATCH_NOALLOC_MAX_WORKSPACE
+    assert lib.moe_dispatch_workspace_bytes(65536, 8, 512) <= cap
+    assert lib.moe_dispatch_workspace_bytes(131072, 8, 512) > cap
+    assert call(_layout(T=131072, k=8, E=512, C=2048)) == MOE_ERR_UNSUPPORTED
+
+
 def test_mlp_and_combine_reject_invalid_arguments(lib):
     L = _layout()
     assert lib.moe_expert_mlp(FAKE, moe.MOE_BF16, ctypes.byref(L), FAKE, FAKE, 0, FAKE, FAKE, 1 << 30,
