@@ -143,12 +143,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void mlp_plan_kernel(const int* __res
 // ------------------------------------------------------------------------------------------------
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
-#ifndef MOE_K_ROTATE
-#define MOE_K_ROTATE 1
-#endif
-#ifndef MOE_GEMM_MIN_WAVES
-#define MOE_GEMM_MIN_WAVES 1
-#endif
+constexpr bool kKRotate = true;
+
 
 struct GemmArgs {
   const void* A;        // activations: send_buf (gate/up) or h (down)
@@ -234,13 +230,11 @@ __global__ __launch_bounds__(256) void fp8_rows_to_bf16_kernel(const uint8_t* __
 // starting stage recovers it (the 28 KB rows of Mixtral's down weights: 3-4 % faster). Tiles that share
 // weights (the M tiles of one expert and N tile) get the same rotation, so they keep sharing them
 // through L2.
-#ifndef MOE_K_ROT_STRIDE
-#define MOE_K_ROT_STRIDE 7
-#endif
+constexpr int kKRotStride = 7;
 __device__ __forceinline__ int k_rotation(int on, int l, int n_tiles, int nt, int nk) {
-  return on ? (int)(((int64_t)l * n_tiles + nt) * MOE_K_ROT_STRIDE % nk) : 0;
+  return on ? (int)(((int64_t)l * n_tiles + nt) * kKRotStride % nk) : 0;
 }
-inline int k_rotate_for(int K, int elem_bytes) { return MOE_K_ROTATE && ((int64_t)K * elem_bytes) % 4096 == 0; }
+inline int k_rotate_for(int K, int elem_bytes) { return kKRotate && ((int64_t)K * elem_bytes) % 4096 == 0; }
 
 // The plan's per-expert row and M-tile starts in LDS (row_start[0..El], tile_start[0..El]), by every
 // workgroup of NTH threads; returns the number of M tiles. With a plan they are copied from it. Without
@@ -681,7 +675,7 @@ struct RegTile {
 
 template <typename T, typename Op, int BM, int BN, int BK, int WM, int WN, bool GATED, int RS, int LDB, bool BNT,
           bool BUF, bool COMBINE = false>
-__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(MOE_GEMM_MIN_WAVES)))
+__global__ __launch_bounds__(WM* WN * 64) __attribute__((amdgpu_waves_per_eu(1)))
 void mlp_gemm_kernel(GemmArgs args) {
   static_assert(!COMBINE || !GATED, "the combine follows the down GEMM");
   using Tile = RegTile<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, BUF, COMBINE>;
@@ -1013,9 +1007,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
 // Chunks are XOR-swizzled in LDS as in the other direct-to-LDS kernel (chunk c of row r at c ^ ((r >> 1)
 // & 7)), so the 32-row fragment reads hit distinct banks. Requires K % 64 == 0 and operand buffers below
 // 2 GiB.
-#ifndef MOE_PP_KPH
-#define MOE_PP_KPH 2
-#endif
+constexpr int kPpKph = 2;
 // calls f(std::integral_constant<int, i>) for i = 0 .. N - 1 (compile-time loop index)
 template <int N, int I = 0, typename Fn>
 __device__ __forceinline__ void static_for(Fn&& f) {
@@ -1039,7 +1031,7 @@ __global__ __launch_bounds__(512) void mlp_gemm_pp_kernel(GemmArgs args, int a_b
   constexpr int NACC = GATED ? 2 * TN : TN;
   constexpr int OUT_COLS = GATED ? BN / 2 : BN;
   constexpr int KSTEPS = BK / Op::KS;
-  constexpr int KPH = MOE_PP_KPH, UPS = KSTEPS / KPH;  // K steps per phase, phases per stage and group
+  constexpr int KPH = kPpKph, UPS = KSTEPS / KPH;  // K steps per phase, phases per stage and group
   static_assert(KSTEPS % KPH == 0, "phases split a stage evenly");
   constexpr int OUT_BYTES = BM * OUT_COLS * 2;
   constexpr int SMEM = (2 * STAGE > OUT_BYTES + BM * 4 ? 2 * STAGE : OUT_BYTES + BM * 4);
@@ -1279,123 +1271,56 @@ void launch_gemm(const GemmArgs& a, int grid, hipStream_t stream) {
     mlp_gemm_kernel<T, Op, BM, BN, BK, WM, WN, GATED, RS, LDB, BNT, false, COMBINE><<<grid, WM * WN * 64, 0, stream>>>(a);
 }
 
-// Persistent grid sizes in workgroups per CU and the compute-bound tile shapes; overridable at compile
-// time for tuning sweeps.
-#ifndef MOE_DEC_WPC
-#define MOE_DEC_WPC 3
-#endif
-#ifndef MOE_PRE_WPC
-#define MOE_PRE_WPC 1
-#endif
+// Persistent grid sizes in workgroups per CU, and the register-staged compute-bound tile (the fallback for
+// shapes the direct-to-LDS kernels do not take).
+constexpr int kDecWpc = 3;
+constexpr int kPreWpc = 1;
 // many-rows-per-expert (compute-bound) tiles: BM x BN x BK with WM x WN waves
-#ifndef MOE_PRE_BM
-#define MOE_PRE_BM 128
-#endif
-#ifndef MOE_PRE_BN
-#define MOE_PRE_BN 256
-#endif
-#ifndef MOE_PRE_BK
-#define MOE_PRE_BK 64
-#endif
-#ifndef MOE_PRE_WM
-#define MOE_PRE_WM 2
-#endif
-#ifndef MOE_PRE_WN
-#define MOE_PRE_WN 4
-#endif
+constexpr int kPreBm = 128;
+constexpr int kPreBn = 256;
+constexpr int kPreBk = 64;
+constexpr int kPreWm = 2;
+constexpr int kPreWn = 4;
 
-#ifndef MOE_PRE_OP
-#define MOE_PRE_OP Op32
-#endif
+
 // register stages of global prefetch in flight
-#ifndef MOE_PRE_RS
-#define MOE_PRE_RS 2
-#endif
-#ifndef MOE_DEC_RS
-#define MOE_DEC_RS 2
-#endif
-#ifndef MOE_DEC_DN_RS
-#define MOE_DEC_DN_RS MOE_DEC_RS
-#endif
-#ifndef MOE_PRE_LDB
-#define MOE_PRE_LDB 2
-#endif
-// direct-to-LDS compute-bound kernel: on/off, LDS row swizzle, grid (workgroups per CU), and its two
-// tile shapes: BM x BN x BK with WM x WN waves and NS LDS stages. The tall (256-row) tile does twice the
-// MFMA work per byte staged and per barrier; it is used when every local expert can hold at least
-// MOE_DL_TALL_MIN_ROWS rows, so the ragged last tile of an expert wastes little.
-#ifndef MOE_PRE_DL
-#define MOE_PRE_DL 1
-#endif
-#ifndef MOE_DL_SWZ
-#define MOE_DL_SWZ 1
-#endif
-#ifndef MOE_DL_WPC
-#define MOE_DL_WPC 1
-#endif
-#ifndef MOE_DL_BK
-#define MOE_DL_BK 64
-#endif
-#ifndef MOE_DL_TALL_MIN_ROWS
-#define MOE_DL_TALL_MIN_ROWS 1024
-#endif
+constexpr int kPreRs = 2;
+constexpr int kDecRs = 2;
+constexpr int kDecDnRs = kDecRs;
+constexpr int kPreLdb = 2;
+// Many rows per expert (operands loaded straight into LDS), by the capacity per local expert:
+//   >= kDlTallMinRows  256 x 256 tiles, ping-pong wave schedule (twice the MFMA work per byte staged of a
+//                      128-row tile; an expert's ragged last tile wastes little)
+//   256 .. 1023        320 x 256 tiles: one M tile holds a whole expert of up to 320 rows, so its weights are
+//                      read once (waves skip the 32-row blocks past the tile's rows)
+//   128 .. 255         128 x 256 tiles
+// BK-deep stages, WM x WN waves, NS LDS stages; one workgroup per CU (kDlWpc), LDS row swizzle kDlSwz.
+constexpr bool kPreDl = true;
+constexpr int kDlSwz = 1;
+constexpr int kDlWpc = 1;
+constexpr int kDlBk = 64;
+constexpr int kDlTallMinRows = 1024;
 // 128-row tile
-#ifndef MOE_DL_BN
-#define MOE_DL_BN 256
-#endif
-#ifndef MOE_DL_WM
-#define MOE_DL_WM 2
-#endif
-#ifndef MOE_DL_WN
-#define MOE_DL_WN 4
-#endif
-#ifndef MOE_DL_NS
-#define MOE_DL_NS 3
-#endif
-#ifndef MOE_DL_SPREAD
-#define MOE_DL_SPREAD true
-#endif
-// 256-row tile
-#ifndef MOE_DLT_BN
-#define MOE_DLT_BN 256
-#endif
-#ifndef MOE_DLT_WM
-#define MOE_DLT_WM 4
-#endif
-#ifndef MOE_DLT_WN
-#define MOE_DLT_WN 2
-#endif
-#ifndef MOE_DLT_NS
-#define MOE_DLT_NS 2
-#endif
-#ifndef MOE_DLT_SPREAD
-#define MOE_DLT_SPREAD false
-#endif
-#ifndef MOE_DEC_LDB
-#define MOE_DEC_LDB 1
-#endif
+constexpr int kDlBn = 256;
+constexpr int kDlWm = 2;
+constexpr int kDlWn = 4;
+constexpr int kDlNs = 3;
+constexpr bool kDlSpread = true;
+// 256-row tiles (ping-pong schedule): 256 weight rows per tile
+constexpr int kPpBn = 256;
+constexpr int kDecLdb = 1;
 // few-rows-per-expert (weight streaming) tiles: 32 or 64 rows, BN weight rows, BK deep. 64-row tiles
-// are used when the capacity per local expert is at least MOE_DEC_TALL_MIN_ROWS rows: an expert then
+// are used when the capacity per local expert is at least kDecTallMinRows rows: an expert then
 // often holds more than 32 rows, and one 64-row tile streams its weights once where two 32-row tiles
 // would stream them twice.
-#ifndef MOE_DEC_TALL_MIN_ROWS
-#define MOE_DEC_TALL_MIN_ROWS 32
-#endif
-#ifndef MOE_DEC_GU_BN
-#define MOE_DEC_GU_BN 128
-#endif
-#ifndef MOE_DEC_GU_BK
-#define MOE_DEC_GU_BK 64
-#endif
-#ifndef MOE_DEC_DN_BN
-#define MOE_DEC_DN_BN 64
-#endif
-#ifndef MOE_DEC_DN_BK
-#define MOE_DEC_DN_BK 128
-#endif
-constexpr int DEC_GU_WN = MOE_DEC_GU_BN / 32 < 4 ? MOE_DEC_GU_BN / 32 : 4;
-constexpr int DEC_DN_WN = MOE_DEC_DN_BN / 16 < 4 ? MOE_DEC_DN_BN / 16 : 4;
-using PreOp = MOE_PRE_OP;
+constexpr int kDecTallMinRows = 32;
+constexpr int kDecGuBn = 128;
+constexpr int kDecGuBk = 64;
+constexpr int kDecDnBn = 64;
+constexpr int kDecDnBk = 128;
+constexpr int DEC_GU_WN = kDecGuBn / 32 < 4 ? kDecGuBn / 32 : 4;
+constexpr int DEC_DN_WN = kDecDnBn / 16 < 4 ? kDecDnBn / 16 : 4;
+using PreOp = Op32;
 
 
 // wpc = 0: one workgroup per tile of the worst-case tile count (workgroups past the real tile count
@@ -1420,13 +1345,11 @@ bool dl_fits(int64_t rows_max, int H, int F) {
   const int64_t lim = 0x7ffffff0ll - 256;
   const int64_t send_bytes = rows_max * (int64_t)H * 2, h_bytes = rows_max * (int64_t)F * 2;
   const int64_t wgu_bytes = (int64_t)2 * F * H * 2, wdn_bytes = (int64_t)H * F * 2;
-  return MOE_PRE_DL && H % MOE_DL_BK == 0 && F % MOE_DL_BK == 0 && send_bytes < lim && h_bytes < lim &&
+  return kPreDl && H % kDlBk == 0 && F % kDlBk == 0 && send_bytes < lim && h_bytes < lim &&
          wgu_bytes < lim && wdn_bytes < lim;
 }
 
-#ifndef MOE_PP
-#define MOE_PP 1
-#endif
+
 template <int BM, int BN, int WM, int WN, bool COMBINE>
 void launch_pp(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
                int64_t h_bytes, int num_cus, hipStream_t stream) {
@@ -1439,11 +1362,11 @@ void launch_pp(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H
 template <int BM, int BN, int WM, int WN, int NS, bool SPREAD, bool COMBINE>
 void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
                int64_t h_bytes, int num_cus, hipStream_t stream) {
-  const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, BN / 2), num_cus, MOE_DL_WPC);
-  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, true, NS, MOE_DL_SWZ, SPREAD><<<g1, WM * WN * 64, 0, stream>>>(
+  const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, BN / 2), num_cus, kDlWpc);
+  mlp_gemm_dl_kernel<BM, BN, kDlBk, WM, WN, true, NS, kDlSwz, SPREAD><<<g1, WM * WN * 64, 0, stream>>>(
       gu, (int)send_bytes);
-  const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, BN), num_cus, MOE_DL_WPC);
-  mlp_gemm_dl_kernel<BM, BN, MOE_DL_BK, WM, WN, false, NS, MOE_DL_SWZ, SPREAD, COMBINE><<<g2, WM * WN * 64, 0, stream>>>(
+  const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, BN), num_cus, kDlWpc);
+  mlp_gemm_dl_kernel<BM, BN, kDlBk, WM, WN, false, NS, kDlSwz, SPREAD, COMBINE><<<g2, WM * WN * 64, 0, stream>>>(
       dn, (int)h_bytes);
 }
 
@@ -1453,11 +1376,11 @@ void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, i
   // every weight byte is read by one tile only, so both GEMMs stream the weights with non-temporal
   // loads: Mixtral-shaped gate/up 350 -> 324 us and down 174 -> 165 us, the Kimi-share down GEMM
   // 235 -> 224 us (interleaved pairs on one GPU)
-  const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_DEC_GU_BN / 2), num_cus, MOE_DEC_WPC);
-  launch_gemm<bf16_t, Op16, BM, MOE_DEC_GU_BN, MOE_DEC_GU_BK, 1, DEC_GU_WN, true, MOE_DEC_RS, MOE_DEC_LDB, true>(
+  const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, kDecGuBn / 2), num_cus, kDecWpc);
+  launch_gemm<bf16_t, Op16, BM, kDecGuBn, kDecGuBk, 1, DEC_GU_WN, true, kDecRs, kDecLdb, true>(
       gu, g1, stream);
-  const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_DEC_DN_BN), num_cus, MOE_DEC_WPC);
-  launch_gemm<bf16_t, Op16, BM, MOE_DEC_DN_BN, MOE_DEC_DN_BK, 1, DEC_DN_WN, false, MOE_DEC_DN_RS, MOE_DEC_LDB, true,
+  const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, kDecDnBn), num_cus, kDecWpc);
+  launch_gemm<bf16_t, Op16, BM, kDecDnBn, kDecDnBk, 1, DEC_DN_WN, false, kDecDnRs, kDecLdb, true,
               COMBINE>(dn, g2, stream);
 }
 }  // namespace
@@ -1468,9 +1391,9 @@ void launch_decode(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, i
 MlpTiles mlp_pick_tiles(int64_t rows_max, int El, int H, int F, int xdt_bf16) {
   if (!xdt_bf16) return MlpTiles{32, 2};
   const int64_t per_expert = El > 0 ? rows_max / El : rows_max;
-  if (per_expert < 128) return per_expert >= MOE_DEC_TALL_MIN_ROWS ? MlpTiles{64, 5} : MlpTiles{32, 1};
-  if (!dl_fits(rows_max, H, F)) return MlpTiles{MOE_PRE_BM, 0};
-  if (per_expert >= MOE_DL_TALL_MIN_ROWS) return MlpTiles{256, 4};
+  if (per_expert < 128) return per_expert >= kDecTallMinRows ? MlpTiles{64, 5} : MlpTiles{32, 1};
+  if (!dl_fits(rows_max, H, F)) return MlpTiles{kPreBm, 0};
+  if (per_expert >= kDlTallMinRows) return MlpTiles{256, 4};
   if (per_expert >= 256) return MlpTiles{320, 6};
   return MlpTiles{128, 3};
 }
@@ -1481,12 +1404,12 @@ bool mlp_reads_plan(const MlpTiles& tiles) { return tiles.variant == 3 || tiles.
 
 int mlp_down_cols(const MlpTiles& tiles) {
   switch (tiles.variant) {
-    case 3: return MOE_DL_BN;
-    case 4: return MOE_DLT_BN;
+    case 3: return kDlBn;
+    case 4: return kPpBn;
     case 6: return 256;
-    case 0: return MOE_PRE_BN;
+    case 0: return kPreBn;
     case 1:
-    case 5: return MOE_DEC_DN_BN;
+    case 5: return kDecDnBn;
     default: return 64;  // fp32
   }
 }
@@ -1496,33 +1419,25 @@ template <bool COMBINE>
 void launch_gemms(const GemmArgs& gu, const GemmArgs& dn, const MlpTiles& tiles, int64_t max_mtiles, int64_t rows_max,
                   int H, int F, int num_cus, hipStream_t stream) {
   switch (tiles.variant) {
-    case 3:
-      if (MOE_PP)
-        launch_pp<128, 512, 2, 4, COMBINE>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
-                                           rows_max * (int64_t)F * 2, num_cus, stream);
-      else
-        launch_dl<128, MOE_DL_BN, MOE_DL_WM, MOE_DL_WN, MOE_DL_NS, MOE_DL_SPREAD, COMBINE>(
-            gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
+    case 3:  // 128 x 256 direct-to-LDS tiles
+      launch_dl<128, kDlBn, kDlWm, kDlWn, kDlNs, kDlSpread, COMBINE>(
+          gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
       break;
-    case 4:
-      if (MOE_PP)
-        launch_pp<256, 256, 4, 2, COMBINE>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
+    case 4:  // 256 x 256 tiles with the ping-pong wave schedule
+      launch_pp<256, kPpBn, 4, 2, COMBINE>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
                                            rows_max * (int64_t)F * 2, num_cus, stream);
-      else
-        launch_dl<256, MOE_DLT_BN, MOE_DLT_WM, MOE_DLT_WN, MOE_DLT_NS, MOE_DLT_SPREAD, COMBINE>(
-            gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2, num_cus, stream);
       break;
     case 6:  // one 320-row tile holds a whole expert of up to 320 rows: its weights are read once
       launch_dl<320, 256, 2, 4, 2, false, COMBINE>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
                                                    rows_max * (int64_t)F * 2, num_cus, stream);
       break;
     case 0: {  // bf16, many rows per expert, operands staged through registers
-      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, MOE_PRE_BN / 2), num_cus, MOE_PRE_WPC);
-      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, true, MOE_PRE_RS,
-                  MOE_PRE_LDB, false>(gu, g1, stream);
-      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, MOE_PRE_BN), num_cus, MOE_PRE_WPC);
-      launch_gemm<bf16_t, PreOp, MOE_PRE_BM, MOE_PRE_BN, MOE_PRE_BK, MOE_PRE_WM, MOE_PRE_WN, false, MOE_PRE_RS,
-                  MOE_PRE_LDB, false, COMBINE>(dn, g2, stream);
+      const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, kPreBn / 2), num_cus, kPreWpc);
+      launch_gemm<bf16_t, PreOp, kPreBm, kPreBn, kPreBk, kPreWm, kPreWn, true, kPreRs,
+                  kPreLdb, false>(gu, g1, stream);
+      const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, kPreBn), num_cus, kPreWpc);
+      launch_gemm<bf16_t, PreOp, kPreBm, kPreBn, kPreBk, kPreWm, kPreWn, false, kPreRs,
+                  kPreLdb, false, COMBINE>(dn, g2, stream);
       break;
     }
     case 1:  // bf16, few rows per expert: stream the weights through 32- or 64-row tiles

@@ -21,15 +21,9 @@ namespace moe {
 
 namespace {
 
-#ifndef ROUTE_MAX_SPLITS
-#define ROUTE_MAX_SPLITS 16
-#endif
-#ifndef ROUTE_FUSED_MAX_T
-#define ROUTE_FUSED_MAX_T 4096
-#endif
-#ifndef ROUTE_TOPK_WIDE_MAX_T
-#define ROUTE_TOPK_WIDE_MAX_T 1024
-#endif
+constexpr int kRouteMaxSplits = 16;
+constexpr int kRouteFusedMaxT = 4096;
+constexpr int kRouteTopkWideMaxT = 1024;
 
 constexpr int RG_BM = 64;   // tokens per tile
 constexpr int RG_BN = 64;   // experts per tile
@@ -642,7 +636,7 @@ RouteTiles route_tiles(int T, int xdt_bf16) {
   return RouteTiles{64, 64};
 }
 
-bool route_fused(int T, int E) { return E <= 16 && T <= ROUTE_FUSED_MAX_T; }
+bool route_fused(int T, int E) { return E <= 16 && T <= kRouteFusedMaxT; }
 
 int route_splits(int T, int H, int E, int xdt_bf16, int num_cus) {
   if (route_fused(T, E)) return 1;
@@ -652,7 +646,7 @@ int route_splits(int T, int H, int E, int xdt_bf16, int num_cus) {
   // at least 256 K per split, and few enough splits that the partial sums stay a small share of the
   // traffic (the top-k kernel reads them all back)
   int smax = H / 256 > 0 ? H / 256 : 1;
-  if (smax > ROUTE_MAX_SPLITS) smax = ROUTE_MAX_SPLITS;
+  if (smax > kRouteMaxSplits) smax = kRouteMaxSplits;
   if (s > smax) s = smax;
   if (s < 1) s = 1;
   return s;
@@ -700,11 +694,11 @@ hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, cons
     const uintptr_t al = reinterpret_cast<uintptr_t>(partial) | reinterpret_cast<uintptr_t>(logits);
     const int blocks = ceil_div_host(T, 4);  // four tokens (waves) per workgroup
     // with few tokens every split is loaded at once (latency); with many, four at a time (occupancy)
-    const bool wide = T <= ROUTE_TOPK_WIDE_MAX_T;
+    const bool wide = T <= kRouteTopkWideMaxT;
 #define MOE_ROUTE_ROWS(VW)                                                                                       \
   do {                                                                                                         \
     if (wide)                                                                                                  \
-      route_topk_rows_kernel<VW, ROUTE_MAX_SPLITS><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, \
+      route_topk_rows_kernel<VW, kRouteMaxSplits><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, \
                                                                                T, E, k, logits, ids, wts);      \
     else                                                                                                       \
       route_topk_rows_kernel<VW, 4><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k,    \
