@@ -181,7 +181,7 @@ def algorithmic_bytes(cfg, C, counts, s, fp8=False, sender=False):
                 route_flops=2 * T * E * H, mlp_flops=6 * H * F * kept)
 
 
-def cpu_baseline(cfg, inp_dev, fp8=False, min_seconds=10.0, max_seconds=30.0, max_mlp_experts=8):
+def cpu_baseline(cfg, inp_dev, fp8=False, min_seconds=10.0, max_seconds=30.0, max_mlp_experts=32):
     """Time the CPU oracle (as it stands) on the same workload, stage by stage.
 
     Route, dispatch and combine run on the whole batch, so the capacity, the drops and the rows are the
@@ -189,7 +189,7 @@ def cpu_baseline(cfg, inp_dev, fp8=False, min_seconds=10.0, max_seconds=30.0, ma
     max_mlp_experts, evenly spaced; one expert's weights on the host at a time) and its time is scaled to
     all active local experts by the mean time per sampled expert. Combine reads the dispatched rows in
     place of expert outputs (its cost does not depend on the values). The whole sequence repeats until
-    about min_seconds of oracle work (never past max_seconds)."""
+    about min_seconds of measured oracle work (never past max_seconds)."""
     import numpy as np
     import torch
 
@@ -215,8 +215,8 @@ def cpu_baseline(cfg, inp_dev, fp8=False, min_seconds=10.0, max_seconds=30.0, ma
     wr = host(inp_dev["w_router"])
     C = W.capacity(cfg, T)
     stages = {"route": 0.0, "dispatch": 0.0, "expert_mlp": 0.0, "combine": 0.0}
-    runs, total = 0, 0.0
-    while runs == 0 or (total < min_seconds and total * (runs + 1) / runs <= max_seconds):
+    runs, total, work = 0, 0.0, 0.0  # estimated layer seconds; measured oracle seconds
+    while runs == 0 or (work < min_seconds and work * (runs + 1) / runs <= max_seconds):
         t0 = time.perf_counter()
         logits = oracle.router_logits(x, dt, wr, bias)
         ids, w = oracle.topk_softmax(logits, k)
@@ -252,14 +252,15 @@ def cpu_baseline(cfg, inp_dev, fp8=False, min_seconds=10.0, max_seconds=30.0, ma
         stages["expert_mlp"] += mlp_est
         stages["combine"] += t4 - t3
         total += (t1 - t0) + (t2 - t1) + mlp_est + (t4 - t3)
+        work += (t1 - t0) + (t2 - t1) + mlp_s + (t4 - t3)
         runs += 1
     what = " with fp8 dispatch" if fp8 else ""
     sample = (f"the whole {cfg.name} batch ({T} tokens, capacity {C}, {lay.total} kept rows){what}: route, dispatch "
               f"and combine on every token; the expert MLP on all {mlp_rows} rows of {len(picks)} of the "
               f"{len(active)} active local experts (evenly spaced), scaled by the mean time per expert; "
-              f"{runs} run{'s' if runs > 1 else ''}")
+              f"{runs} run{'s' if runs > 1 else ''}, {work:.1f} s of oracle work")
     return dict(value=T * runs / total, unit="tokens/s", cores=int(threads), kind="oracle", sample=sample,
-                seconds_per_layer=round(total / runs, 3),
+                seconds_per_layer=round(total / runs, 3), oracle_seconds=round(work, 2),
                 stages_s={n: round(v / runs, 3) for n, v in stages.items()}, runs=runs,
                 mlp_sample={"experts": int(len(picks)), "rows": int(mlp_rows), "active_local_experts": int(len(active))})
 

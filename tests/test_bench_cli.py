@@ -48,5 +48,6 @@ def test_cpu_baseline_runs_the_whole_batch_and_samples_experts():
     r = bench.cpu_baseline(cfg, inp, min_seconds=0.0)
     assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0 and r["cores"] >= 1
     assert set(r["stages_s"]) == {"route", "dispatch", "expert_mlp", "combine"}
-    assert r["mlp_sample"]["experts"] == 8 and r["mlp_sample"]["active_local_experts"] == 256
+    assert r["mlp_sample"]["experts"] == 32 and r["mlp_sample"]["active_local_experts"] == 256
+    assert r["oracle_seconds"] > 0
     assert "16384 tokens, capacity 512" in r["sample"]
