@@ -27,9 +27,10 @@
 //                         on v_mfma_f32_16x16x32_bf16), fp32 (v_mfma_f32_16x16x4_f32), and the bf16
 //                         fallback for shapes the other family does not take.
 //     mlp_gemm_dl_kernel  many rows per expert: operands go global -> LDS directly (buffer loads with
-//                         the LDS bit), NS LDS stages in flight, 128- or 320-row tiles on
-//                         v_mfma_f32_32x32x16_bf16, epilogue staged through LDS; the 320-row tile runs
-//                         the cross-stage schedule (two slots, loads interleaved with the MFMAs).
+//                         the LDS bit), NS LDS stages in flight, 128-row tiles on
+//                         v_mfma_f32_32x32x16_bf16, epilogue staged through LDS.
+//     mlp_gemm_xs_kernel  the same loads for 320-row tiles that hold a whole expert: two stage slots,
+//                         loads interleaved with the MFMAs, the next tile's first stage prefetched.
 //     mlp_gemm_pp_kernel  256-row tiles for experts of 1024+ rows: two wave groups alternate between
 //                         loading and multiplying (ping-pong).
 //   All accumulate in fp32.
@@ -737,8 +738,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool GATED, int NS, int SWZ, bool SPREAD, bool COMBINE = false,
-          bool XS = false>
+template <int BM, int BN, int BK, int WM, int WN, bool GATED, int NS, int SWZ, bool SPREAD, bool COMBINE = false>
 __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args, int a_bytes) {
   static_assert(!COMBINE || !GATED, "the combine follows the down GEMM");
   using Op = Op32;
@@ -750,9 +750,6 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
   constexpr int A_INS = BM / RPI, B_INS = BN / RPI;  // 1 KB wave loads per stage
   static_assert((A_INS + B_INS) % NW == 0, "wave loads must split evenly");
   constexpr int LPW = (A_INS + B_INS) / NW;
-  // the cross-stage schedule (XS, below) gives every wave AW A loads and BW B loads per stage
-  static_assert(!XS || (NS == 2 && BK == 64 && A_INS % NW == 0 && B_INS % NW == 0), "XS: two 64-deep slots");
-  constexpr int AW = XS ? A_INS / NW : 0, BW = XS ? B_INS / NW : 0;
   constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
   constexpr int WTM = BM / WM, TM = WTM / S;
   constexpr int TN = GATED ? (BN / 2 / WN) / S : (BN / WN) / S;
@@ -814,21 +811,17 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
     // this wave's LPW load instructions per stage: byte offset (without k) and LDS offset of each.
     // The source rows of the A instructions are looked up first, unconditionally (rows past the tile
     // read its last row), so the lookups are in flight together rather than one wait each.
-    // the 1 KB load instruction behind this wave's load q: with XS, loads 0..AW-1 are A instructions and
-    // the rest B instructions (so whether a load reads A or B is known at compile time); otherwise the
-    // wave takes LPW consecutive instructions
-    auto ins_of = [&](int q) { return XS ? (q < AW ? wave * AW + q : A_INS + wave * BW + (q - AW)) : wave * LPW + q; };
     int srcs[LPW];
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
-      const int p = p0 + min(ins_of(q) * RPI + lane / CPR, m_rows - 1);
-      srcs[q] = (args.a_perm && ins_of(q) < A_INS) ? args.a_perm[p] : p;
+      const int p = p0 + min((wave * LPW + q) * RPI + lane / CPR, m_rows - 1);
+      srcs[q] = (args.a_perm && wave * LPW + q < A_INS) ? args.a_perm[p] : p;
     }
     int voff[LPW], loff[LPW];
     bool isa[LPW];
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
-      const int ins = ins_of(q);
+      const int ins = wave * LPW + q;
       const int r_in = lane / CPR, pos = lane % CPR;
       if (ins < A_INS) {
         const int r = ins * RPI + r_in;
@@ -866,13 +859,6 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
       }
     };
     auto issue = [&](int st, int slot) { issue_part(st, slot, 0, 1); };
-    // XS: this wave's load q (a compile-time index) of stage st into slot
-    auto issue_one = [&](int st, int slot, int q) {
-      const int vo = voff[q] == OOB ? OOB : voff[q] + st * BK * 2;
-      auto* dst = (__attribute__((address_space(3))) void*)(smem + slot * STAGE + loff[q]);
-      if (q < AW) __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, vo, 0, 0, 0);
-      else __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dst, 16, vo, 0, 0, 0);
-    };
 
     typename Op::Acc acc[TM][NACC];
 #pragma unroll
@@ -894,9 +880,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int r = wm * WTM + i * S + fr;
-        // (XS reads every block unconditionally, so the LDS-read counts the compiler waits on are static;
-        // rows past the tile hold zeros)
-        if (XS || i < mb) af[i][0] = ld16(base + r * ROWB + ((c ^ dl_swz<SWZ, CPR>(r)) << 4));
+        if (i < mb) af[i][0] = ld16(base + r * ROWB + ((c ^ dl_swz<SWZ, CPR>(r)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < NACC; ++j) {
@@ -934,71 +918,6 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
     // earlier stores of this wave are done and every wave is done with the LDS of the previous tile
     wait_vmcnt<0>();
     lds_barrier();
-    if constexpr (XS) {
-      // Cross-stage schedule over two slots (stage s in slot s & 1). The barrier that publishes stage
-      // s + 1 sits before the MFMAs of stage s's last K step, whose fragments are already in registers:
-      // those MFMAs then cover the barrier's skew and the fragment reads of stage s + 1's first K step.
-      // Right after that barrier stage s's slot is free, and it takes the B loads of stage s + 2, one
-      // between each pair of MFMAs of that last K step (a full stage ahead of their use); the A loads of
-      // stage s + 1 (L2-resident rows, shorter latency) go out between the MFMAs of stage s's first K
-      // step. Loads leave one at a time instead of a 72-load burst per stage behind the barrier, which
-      // stalled every wave's MFMA issue until the address unit had taken the burst.
-      constexpr int KSTEPS = BK / Op::KS;
-#pragma unroll
-      for (int q = 0; q < BW; ++q) issue_one(0, 0, AW + q);
-#pragma unroll
-      for (int q = 0; q < AW; ++q) issue_one(0, 0, q);
-      if (nk > 1) {
-#pragma unroll
-        for (int q = 0; q < BW; ++q) issue_one(1, 1, AW + q);
-        wait_vmcnt<BW>();  // stage 0 (issued first) has landed
-      } else {
-        wait_vmcnt<0>();
-      }
-      lds_barrier();
-      u32x4 af[2][TM][1], bfg[2][NACC][1];
-      load_frags(smem, 0, af[0], bfg[0]);
-      // one stage; HAVE1 / HAVE2: stages s + 1 / s + 2 exist (compile-time, so the steady-state loop
-      // carries no branches on them)
-      auto stage = [&](int s, auto HAVE1, auto HAVE2) {
-        constexpr bool have1 = decltype(HAVE1)::value, have2 = decltype(HAVE2)::value;
-        const int slot = s & 1;
-        const unsigned char* base = smem + slot * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          if (ks + 1 < KSTEPS) {
-            load_frags(base, (ks + 1) * Op::KS, af[(ks + 1) & 1], bfg[(ks + 1) & 1]);
-          } else if (have1) {
-            wait_vmcnt<0>();  // this wave's loads of stage s + 1 (nothing younger is in flight)
-            lds_barrier();    // stage s + 1 visible to every wave; no wave reads slot s & 1 any more
-            load_frags(smem + (slot ^ 1) * STAGE, 0, af[0], bfg[0]);
-          }
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            if (i < mb) {
-#pragma unroll
-              for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[ks & 1][i], bfg[ks & 1][j]);
-            }
-            if (ks == 0 && i < AW && have1) issue_one(s + 1, slot ^ 1, i);
-            if (ks == KSTEPS - 1 && i < BW && have2) issue_one(s + 2, slot, AW + i);
-          }
-          if (ks == 0 && have1) {
-#pragma unroll
-            for (int q = TM; q < AW; ++q) issue_one(s + 1, slot ^ 1, q);
-          }
-          if (ks == KSTEPS - 1 && have2) {
-#pragma unroll
-            for (int q = TM; q < BW; ++q) issue_one(s + 2, slot, AW + q);
-          }
-        }
-      };
-      using Yes = std::integral_constant<bool, true>;
-      using No = std::integral_constant<bool, false>;
-      int s = 0;
-      for (; s + 2 < nk; ++s) stage(s, Yes{}, Yes{});
-      if (s + 1 < nk) stage(s++, Yes{}, No{});
-      stage(s, No{}, No{});
-    } else {
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st)
       if (st < nk) issue(st, st);
@@ -1013,7 +932,6 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
       lds_barrier();  // stage s visible to every wave; every wave is done with stage s - 1
       const int next = s + NS - 1 < nk ? s + NS - 1 : -1;
       compute(s % NS, next, next >= 0 ? next % NS : 0);
-    }
     }
 
     // epilogue through LDS, free once every wave is past the last stage: the waves write their bf16
@@ -1076,6 +994,370 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_dl_kernel(GemmArgs args,
       tile_arrive_combine<bf16_t, NW * 64, OUT_COLS>(args, p0, m_rows, n0, nt, n_tiles, reinterpret_cast<int*>(smem));
     }
   }
+}
+
+
+// ------------------------------------------------------------------------------------------------
+// Whole-expert tiles: direct global -> LDS loads, cross-stage schedule, cross-tile prefetch
+// ------------------------------------------------------------------------------------------------
+// The loads and fragment layout of mlp_gemm_dl_kernel (64-deep stages, 1 KB wave loads of 8 rows,
+// XOR-swizzled 16-byte chunks), with two stage slots (stage s in slot s & 1) and this schedule:
+//  - The barrier that publishes stage s + 1 sits before the MFMAs of stage s's last K step, whose
+//    fragments are already in registers; those MFMAs cover the barrier's skew and the fragment reads
+//    of stage s + 1's first K step.
+//  - Right after that barrier stage s's slot is free: it takes the B (weight) loads of stage s + 2, one
+//    between each pair of MFMAs of the last K step, a full stage ahead of their use. The A loads of
+//    stage s + 1 (activation rows, L2-resident, shorter latency) go out between the MFMAs of stage s's
+//    first K step. Every wave issues AW A loads and BW B loads per stage, so whether a load reads A or
+//    B is known at compile time, and no wave waits behind a burst of a whole stage's loads.
+//  - Cross-tile prefetch (even stage counts): the next tile's stage 0 is the continuation of the
+//    pipeline - its B loads go out in stage nk - 2's last K step and its A loads in stage nk - 1's
+//    first, into slot 0, while the output tile is staged through slot 1 and the space past it. The
+//    next tile's expert, rows and A-row lookups are found during stage nk - 2, from a copy of the
+//    plan's per-expert starts in LDS.
+// Requires K % 64 == 0 and operand buffers below 2 GiB (the host falls back otherwise).
+template <int BM, int BN, int WM, int WN, bool GATED, bool COMBINE = false>
+__global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_xs_kernel(GemmArgs args, int a_bytes) {
+  static_assert(!COMBINE || !GATED, "the combine follows the down GEMM");
+  using Op = Op32;
+  constexpr int BK = 64, S = 32, ROWB = BK * 2, CPR = BK / 8, RPI = 64 / CPR;
+  constexpr int NW = WM * WN;
+  constexpr int A_INS = BM / RPI, B_INS = BN / RPI;  // 1 KB wave loads per stage
+  static_assert(A_INS % NW == 0 && B_INS % NW == 0, "every wave issues the same number of A and B loads");
+  constexpr int AW = A_INS / NW, BW = B_INS / NW, LPW = AW + BW;
+  constexpr int A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB;
+  constexpr int WTM = BM / WM, TM = WTM / S;
+  constexpr int TN = GATED ? (BN / 2 / WN) / S : (BN / WN) / S;
+  constexpr int NACC = GATED ? 2 * TN : TN;
+  constexpr int OUT_COLS = GATED ? BN / 2 : BN;
+  constexpr int KSTEPS = BK / Op::KS;
+  static_assert(TM >= 1 && TN >= 1, "wave tile too small");
+  // LDS: slot 0 at 0, slot 1 at STAGE. After the last stage the output tile goes out in OCH column
+  // parts staged from slot 1 on (slot 0 may hold the next tile's stage 0), then the destination rows,
+  // then the plan copy (row starts, M-tile starts).
+  constexpr int OCW = 128, OCH = OUT_COLS / OCW, CPO = OCW / 8;
+  static_assert(OUT_COLS % OCW == 0 && WN % OCH == 0, "output parts");
+  constexpr int STG_OFF = STAGE, OROW_OFF = STG_OFF + BM * OCW * 2, PLAN_OFF = OROW_OFF + BM * 4;
+  constexpr int PLAN_INTS = MOE_MAX_EXPERTS + 1;
+  constexpr int SMEM_END = PLAN_OFF + 2 * PLAN_INTS * 4;
+  constexpr int SMEM = SMEM_END > 2 * STAGE ? SMEM_END : 2 * STAGE;
+  static_assert(PLAN_OFF >= 2 * STAGE || OROW_OFF >= 2 * STAGE, "the plan copy lies past the stage slots");
+  static_assert(SMEM <= 160 * 1024, "LDS");
+  static_assert(BM <= NW * 64 && (BM + 1) * 4 <= BM * OCW * 2, "one row per thread; token list fits");
+  // the kernel's only LDS object (see mlp_gemm_dl_kernel)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  int* s_rs = reinterpret_cast<int*>(smem + PLAN_OFF);  // row start per local expert [0..El]
+  int* s_ts = s_rs + PLAN_INTS;                          // M-tile start per local expert [0..El]
+  int* s_orow = reinterpret_cast<int*>(smem + OROW_OFF);
+
+  const bf16_t* A = static_cast<const bf16_t*>(args.A);
+  const bf16_t* W = static_cast<const bf16_t*>(args.W);
+  bf16_t* __restrict__ Out = static_cast<bf16_t*>(args.Out);
+  const int El = args.El;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int nk = args.K / BK;
+  const int OOB = 0x7ffffff0;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, a_bytes, 0x00020000);
+  const int w_bytes = (int)(args.w_stride * 2);
+  const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
+  const int total = args.plan[0] * n_tiles;
+  for (int i = tid; i <= El; i += NW * 64) {
+    s_rs[i] = args.plan[2 + i];
+    s_ts[i] = args.plan[3 + El + i];
+  }
+  lds_barrier();
+
+  const int G = gridDim.x;
+  int t_begin = blockIdx.x, t_end = total, t_step = G;
+  if ((G & 7) == 0 && G >= 8) {
+    const int x = blockIdx.x & 7, per = (total + 7) >> 3;
+    t_begin = x * per + (blockIdx.x >> 3);
+    t_end = min(total, (x + 1) * per);
+    t_step = G >> 3;
+  }
+  if (t_begin >= t_end) return;
+
+  // a tile's expert, N tile and rows. Tiles list (local expert, N tile, M tile) in expert order and a
+  // workgroup's tiles increase, so the expert is found by scanning on from the previous tile's.
+  struct TileP {
+    int l, nt, p0, m_rows, n0;
+  };
+  auto tile_params = [&](int tile, int l) {
+    while (__builtin_amdgcn_readfirstlane(s_ts[l + 1]) * n_tiles <= tile) ++l;
+    const int ts = __builtin_amdgcn_readfirstlane(s_ts[l]), mt_l = __builtin_amdgcn_readfirstlane(s_ts[l + 1]) - ts;
+    const int local = tile - ts * n_tiles;
+    const int nt = local / mt_l, mt = local % mt_l;
+    TileP t;
+    t.l = l;
+    t.nt = nt;
+    t.p0 = __builtin_amdgcn_readfirstlane(s_rs[l]) + mt * BM;
+    t.m_rows = min(BM, __builtin_amdgcn_readfirstlane(s_rs[l + 1]) - t.p0);
+    t.n0 = nt * OUT_COLS;
+    return t;
+  };
+  // this wave's loads: q < AW are A instructions wave * AW + q, q >= AW are B instructions wave * BW + q - AW;
+  // voff: byte offset without k (OOB past the tile), loff: LDS offset within a slot
+  int voff[LPW];
+  auto a_src_row = [&](const TileP& t, int q) { return t.p0 + min((wave * AW + q) * RPI + lane / CPR, t.m_rows - 1); };
+  auto setup_a = [&](const TileP& t, const int (&src)[AW]) {
+#pragma unroll
+    for (int q = 0; q < AW; ++q) {
+      const int r = (wave * AW + q) * RPI + lane / CPR;
+      const int chunk = (lane % CPR) ^ dl_swz<1, CPR>(r);
+      voff[q] = r < t.m_rows ? src[q] * args.lda * 2 + chunk * 16 : OOB;
+    }
+  };
+  auto lookup_a = [&](const TileP& t, int (&src)[AW]) {
+#pragma unroll
+    for (int q = 0; q < AW; ++q) src[q] = args.a_perm ? args.a_perm[a_src_row(t, q)] : a_src_row(t, q);
+  };
+  auto setup_b = [&](const TileP& t) {
+#pragma unroll
+    for (int q = AW; q < LPW; ++q) {
+      const int r = (wave * BW + q - AW) * RPI + lane / CPR;
+      const int chunk = (lane % CPR) ^ dl_swz<1, CPR>(r);
+      int wrow, ncol;
+      if (GATED) {
+        const int half = r / (BN / 2), rr = r % (BN / 2);
+        ncol = t.n0 + rr;
+        wrow = ncol + half * args.up_offset;
+      } else {
+        ncol = t.n0 + r;
+        wrow = ncol;
+      }
+      voff[q] = ncol < args.N ? wrow * args.K * 2 + chunk * 16 : OOB;
+    }
+  };
+  auto b_rsrc_of = [&](const TileP& t) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)t.l * args.w_stride), (short)0, w_bytes, 0x00020000);
+  };
+  auto loff = [&](int q) { return q < AW ? (wave * AW + q) * 1024 : A_BYTES + (wave * BW + q - AW) * 1024; };
+  __amdgpu_buffer_rsrc_t b_rsrc;
+  // this wave's load q (a compile-time index) of stage st into slot
+  auto issue_one = [&](int st, int slot, int q) {
+    const int vo = voff[q] == OOB ? OOB : voff[q] + st * BK * 2;
+    auto* dst = (__attribute__((address_space(3))) void*)(smem + slot * STAGE + loff(q));
+    if (q < AW) __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, vo, 0, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dst, 16, vo, 0, 0, 0);
+  };
+
+  const int fr = lane & 31, fq = lane >> 5;
+  // fragments of K step kk of the stage at base: every A block (rows past the tile hold zeros), and B
+  auto load_frags = [&](const unsigned char* base, int kk, u32x4 (&af)[TM][1], u32x4 (&bfg)[NACC][1]) {
+    const int c = kk / 8 + fq;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * WTM + i * S + fr;
+      af[i][0] = ld16(base + r * ROWB + ((c ^ dl_swz<1, CPR>(r)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < NACC; ++j) {
+      int r;
+      if (GATED) {
+        const int half = j / TN, jj = j % TN;
+        r = half * (BN / 2) + wn * (BN / 2 / WN) + jj * S + fr;
+      } else {
+        r = wn * (BN / WN) + j * S + fr;
+      }
+      bfg[j][0] = ld16(base + A_BYTES + r * ROWB + ((c ^ dl_swz<1, CPR>(r)) << 4));
+    }
+  };
+
+  // PF: the stage count is even, so every tile's stage 0 is issued by the tile before it (the first
+  // one's before the loop). Every tile then takes the same path, and the loads each wave has in
+  // flight are the same at every point of it (their count must be known where the fragment reads
+  // wait on LDS, or those waits fall back to waiting for everything).
+  auto run = [&](auto PF_C) {
+  constexpr bool PF = decltype(PF_C)::value;
+  TileP cur = tile_params(t_begin, 0);
+  {
+    int src[AW];
+    lookup_a(cur, src);
+    setup_a(cur, src);
+    setup_b(cur);
+    b_rsrc = b_rsrc_of(cur);
+  }
+  if (PF) {
+    wait_vmcnt<0>();  // the A row lookups
+#pragma unroll
+    for (int q = AW; q < LPW; ++q) issue_one(0, 0, q);
+#pragma unroll
+    for (int q = 0; q < AW; ++q) issue_one(0, 0, q);
+  }
+  for (int tile = t_begin; tile < t_end; tile += t_step) {
+    const int next = tile + t_step;
+    const bool has_next = next < t_end;
+    const bool pf = PF && has_next;
+    typename Op::Acc acc[TM][NACC];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < NACC; ++j)
+#pragma unroll
+        for (int q = 0; q < Op::NR; ++q) acc[i][j][q] = 0.f;
+    // 32-row blocks of this wave's rows that hold tile rows (wave-uniform): the others are not multiplied
+    const int mb = min(TM, max(0, (cur.m_rows - wm * WTM + S - 1) / S));
+
+    // earlier stores and loads of this wave are done, and every wave is past the previous tile's LDS use
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (!PF) {
+#pragma unroll
+      for (int q = AW; q < LPW; ++q) issue_one(0, 0, q);
+#pragma unroll
+      for (int q = 0; q < AW; ++q) issue_one(0, 0, q);
+    }
+    if (nk > 1) {
+#pragma unroll
+      for (int q = AW; q < LPW; ++q) issue_one(1, 1, q);
+      wait_vmcnt<BW>();  // everything but stage 1's B loads has landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    u32x4 af[2][TM][1], bfg[2][NACC][1];
+    load_frags(smem, 0, af[0], bfg[0]);
+    TileP nxt = cur;
+    int nsrc[AW];
+
+    // one stage. HAVE1 / HAVE2: stages s + 1 / s + 2 of this tile exist; PRE: 1 for stage nk - 2 and 2
+    // for stage nk - 1, where the next tile's stage 0 goes out when pf
+    auto stage = [&](int s, auto HAVE1, auto HAVE2, auto PRE) {
+      constexpr bool have1 = decltype(HAVE1)::value, have2 = decltype(HAVE2)::value;
+      constexpr int pre = decltype(PRE)::value;
+      const int slot = s & 1;
+      const unsigned char* base = smem + slot * STAGE;
+      if (pre == 2 && pf) setup_a(nxt, nsrc);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        if (ks + 1 < KSTEPS) {
+          load_frags(base, (ks + 1) * Op::KS, af[(ks + 1) & 1], bfg[(ks + 1) & 1]);
+        } else if (have1) {
+          wait_vmcnt<0>();  // this wave's loads of stage s + 1
+          lds_barrier();    // stage s + 1 visible to every wave; no wave reads slot s & 1 any more
+          load_frags(smem + (slot ^ 1) * STAGE, 0, af[0], bfg[0]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if (i < mb) {
+#pragma unroll
+            for (int j = 0; j < NACC; ++j) Op::step(acc[i][j], af[ks & 1][i], bfg[ks & 1][j]);
+          }
+          if (ks == 0 && i < AW && have1) issue_one(s + 1, slot ^ 1, i);
+          if (ks == KSTEPS - 1 && i < BW && have2) issue_one(s + 2, slot, AW + i);
+          // the next tile's stage 0 into slot 0 (slot here is 0 at pre 1 and 1 at pre 2: nk is even)
+          if (pre == 1 && ks == KSTEPS - 1 && i < BW && pf) issue_one(0, 0, AW + i);
+          if (pre == 2 && ks == 0 && i < AW && pf) issue_one(0, 0, i);
+        }
+        if (ks == 0 && have1) {
+#pragma unroll
+          for (int q = TM; q < AW; ++q) issue_one(s + 1, slot ^ 1, q);
+        }
+        if (ks == KSTEPS - 1 && have2) {
+#pragma unroll
+          for (int q = TM; q < BW; ++q) issue_one(s + 2, slot, AW + q);
+        }
+        if (pre == 1 && ks == KSTEPS - 1 && pf) {
+#pragma unroll
+          for (int q = TM; q < BW; ++q) issue_one(0, 0, AW + q);
+        }
+        if (pre == 2 && ks == 0 && pf) {
+#pragma unroll
+          for (int q = TM; q < AW; ++q) issue_one(0, 0, q);
+        }
+        // after stage nk - 2's first K step this tile has issued all its loads: switch the B operand to
+        // the next tile and start the lookups of its A rows (used at stage nk - 1)
+        if (pre == 1 && ks == 0 && pf) {
+          nxt = tile_params(next, cur.l);
+          setup_b(nxt);
+          b_rsrc = b_rsrc_of(nxt);
+          lookup_a(nxt, nsrc);
+        }
+      }
+    };
+    using Yes = std::integral_constant<bool, true>;
+    using No = std::integral_constant<bool, false>;
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using P2 = std::integral_constant<int, 2>;
+    int s = 0;
+    for (; s + 2 < nk; ++s) stage(s, Yes{}, Yes{}, P0{});
+    if (s + 1 < nk) stage(s++, Yes{}, No{}, P1{});
+    stage(s, No{}, No{}, P2{});
+
+    // epilogue: the waves write their bf16 results to the staging area (lane l holds column l % 32,
+    // rows 8*(q/4) + 4*(l/32) + q%4 of each 32x32 block), then every lane stores whole 16-byte row chunks.
+    // Chunk c of staged row r sits at c ^ (4 * ((r >> 2) & 1)): rows r and r + 4 (one instruction) use
+    // different LDS banks.
+    // (stg is STG_OFF through an opaque move: otherwise the compiler hoists all of this lane's staging
+    // addresses out of the tile loop, where they do not fit the registers and go to scratch memory)
+    int stg;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(stg) : "n"(STG_OFF));
+    auto out_off = [&](int r, int cl) {
+      return stg + r * OCW * 2 + (((cl >> 3) ^ (((r >> 2) & 1) << 2)) << 4) + (cl & 7) * 2;
+    };
+    // the destination row of each tile row, looked up once per tile (all in flight together)
+    int my_orow = 0;
+    if (tid < BM) {
+      const int p = cur.p0 + min(tid, cur.m_rows - 1);
+      my_orow = args.out_perm ? args.out_perm[p] : p;
+    }
+    // with the fused combine, Out (below 2 GiB here, like every operand of this kernel) is stored at agent scope
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Out, (short)0, COMBINE ? args.out_bytes : 0, 0x00020000);
+#pragma unroll
+    for (int oc = 0; oc < OCH; ++oc) {
+      lds_barrier();  // slot 1 (or the previous part) is no longer read
+      if (wn / (WN / OCH) == oc) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            const int cl = (GATED ? wn * (BN / 2 / WN) + j * S + fr : wn * (BN / WN) + j * S + fr) - oc * OCW;
+#pragma unroll
+            for (int q = 0; q < Op::NR; ++q) {
+              const int row = wm * WTM + i * S + Op::out_row(lane, q);
+              float v;
+              if (GATED) v = silu_f32(acc[i][j][q]) * acc[i][j + TN][q];
+              else v = acc[i][j][q];
+              *reinterpret_cast<bf16_t*>(smem + out_off(row, cl)) = (bf16_t)v;
+            }
+          }
+        }
+      }
+      if (oc == 0 && tid < BM) s_orow[tid] = my_orow;
+      lds_barrier();
+      for (int idx = tid; idx < BM * CPO; idx += NW * 64) {
+        const int row = idx / CPO, ch = idx % CPO;
+        const int col = cur.n0 + oc * OCW + ch * 8;
+        if (row < cur.m_rows && col < args.N) {
+          const int orow = s_orow[row];
+          if (COMBINE) st16_agent(out_rsrc, (orow * args.ldo + col) * 2, ld16(smem + out_off(row, ch * 8)));
+          else st16(Out + (int64_t)orow * args.ldo + col, ld16(smem + out_off(row, ch * 8)));
+        }
+      }
+    }
+    if (COMBINE) {
+      lds_barrier();  // every wave has read its output chunks before the token list overwrites them
+      tile_arrive_combine<bf16_t, NW * 64, OUT_COLS>(args, cur.p0, cur.m_rows, cur.n0, cur.nt, n_tiles,
+                                                     reinterpret_cast<int*>(smem + STG_OFF));
+    }
+    if (pf) {
+      cur = nxt;
+    } else if (has_next) {
+      cur = tile_params(next, cur.l);
+      int src[AW];
+      lookup_a(cur, src);
+      setup_a(cur, src);
+      setup_b(cur);
+      b_rsrc = b_rsrc_of(cur);
+    }
+  }
+  };
+  if (nk >= 2 && (nk & 1) == 0) run(std::integral_constant<bool, true>{});
+  else run(std::integral_constant<bool, false>{});
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1447,15 +1729,24 @@ void launch_pp(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H
   mlp_gemm_pp_kernel<BM, BN, WM, WN, false, COMBINE><<<g2, 512, 0, stream>>>(dn, (int)h_bytes);
 }
 
-template <int BM, int BN, int WM, int WN, int NS, bool SPREAD, bool COMBINE, bool XS = false>
+template <int BM, int BN, int WM, int WN, int NS, bool SPREAD, bool COMBINE>
 void launch_dl(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
                int64_t h_bytes, int num_cus, hipStream_t stream) {
   const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, BN / 2), num_cus, kDlWpc);
-  mlp_gemm_dl_kernel<BM, BN, kDlBk, WM, WN, true, NS, kDlSwz, SPREAD, false, XS><<<g1, WM * WN * 64, 0, stream>>>(
+  mlp_gemm_dl_kernel<BM, BN, kDlBk, WM, WN, true, NS, kDlSwz, SPREAD><<<g1, WM * WN * 64, 0, stream>>>(
       gu, (int)send_bytes);
   const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, BN), num_cus, kDlWpc);
-  mlp_gemm_dl_kernel<BM, BN, kDlBk, WM, WN, false, NS, kDlSwz, SPREAD, COMBINE, XS><<<g2, WM * WN * 64, 0, stream>>>(
+  mlp_gemm_dl_kernel<BM, BN, kDlBk, WM, WN, false, NS, kDlSwz, SPREAD, COMBINE><<<g2, WM * WN * 64, 0, stream>>>(
       dn, (int)h_bytes);
+}
+
+template <int BM, int BN, int WM, int WN, bool COMBINE>
+void launch_xs(const GemmArgs& gu, const GemmArgs& dn, int64_t max_mtiles, int H, int F, int64_t send_bytes,
+               int64_t h_bytes, int num_cus, hipStream_t stream) {
+  const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, BN / 2), num_cus, 1);
+  mlp_gemm_xs_kernel<BM, BN, WM, WN, true><<<g1, WM * WN * 64, 0, stream>>>(gu, (int)send_bytes);
+  const int g2 = persistent_grid(max_mtiles * ceil_div_host(H, BN), num_cus, 1);
+  mlp_gemm_xs_kernel<BM, BN, WM, WN, false, COMBINE><<<g2, WM * WN * 64, 0, stream>>>(dn, (int)h_bytes);
 }
 
 template <int BM, bool COMBINE>
@@ -1515,11 +1806,12 @@ void launch_gemms(const GemmArgs& gu, const GemmArgs& dn, const MlpTiles& tiles,
       launch_pp<256, kPpBn, 4, 2, COMBINE>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
                                            rows_max * (int64_t)F * 2, num_cus, stream);
       break;
-    case 6:  // one 320-row tile holds a whole expert of up to 320 rows: its weights are read once. The
-             // cross-stage schedule, on 256 experts of 192-512 rows at H 7168, F 2048: gate/up
-             // 4707 -> 4382 us, down 2620 -> 2555 us (same output bits; two kernel traces each)
-      launch_dl<320, 256, 2, 4, 2, false, COMBINE, true>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2,
-                                                         rows_max * (int64_t)F * 2, num_cus, stream);
+    case 6:  // one 320-row tile holds a whole expert of up to 320 rows: its weights are read once. On 256
+             // experts of 192-512 rows at H 7168, F 2048 (same output bits; two kernel traces each):
+             // the cross-stage schedule took gate/up 4707 -> 4382 us and down 2620 -> 2555 us, the
+             // cross-tile prefetch then 4411 -> 4360 and 2562 -> 2528
+      launch_xs<320, 256, 2, 4, COMBINE>(gu, dn, max_mtiles, H, F, rows_max * (int64_t)H * 2, rows_max * (int64_t)F * 2,
+                                         num_cus, stream);
       break;
     case 0: {  // bf16, many rows per expert, operands staged through registers
       const int g1 = persistent_grid(max_mtiles * ceil_div_host(F, kPreBn / 2), num_cus, kPreWpc);
