@@ -97,10 +97,8 @@ int64_t moe_rows_max(int T, int k, int E, int C) {
 
 size_t moe_route_workspace_bytes(int T, int H, int E, moe_dtype_t xdt) {
   if (T <= 0 || H <= 0 || E <= 0 || !valid_dtype(xdt)) return 0;
-  const int splits = moe::route_splits(T, H, E, xdt == MOE_BF16, ROUTE_PLAN_CUS);
-  const int nsplit = moe::ceil_div_host(H, moe::route_k_split(H, splits));
-  if (nsplit <= 1) return 0;
-  return (size_t)nsplit * (size_t)T * (size_t)E * sizeof(float);
+  const moe::RoutePlan plan = moe::route_plan(T, H, E, xdt == MOE_BF16, ROUTE_PLAN_CUS);
+  return plan.planes_bytes + plan.partial_bytes;
 }
 
 int moe_route(const void* x, moe_dtype_t xdt, const float* w_router, const float* logit_bias,
@@ -119,10 +117,9 @@ int moe_route(const void* x, moe_dtype_t xdt, const float* w_router, const float
     return MOE_ERR_INVALID;
   const size_t need = moe_route_workspace_bytes(T, H, E, xdt);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MOE_ERR_INVALID;
-  const int splits = moe::route_splits(T, H, E, xdt == MOE_BF16, ROUTE_PLAN_CUS);
-  float* partial = need > 0 ? static_cast<float*>(workspace) : logits;
+  const moe::RoutePlan plan = moe::route_plan(T, H, E, xdt == MOE_BF16, ROUTE_PLAN_CUS);
   return hip_status(moe::launch_route(x, xdt == MOE_BF16, w_router, logit_bias, logit_bias ? bias_row_stride : 0,
-                                      T, H, E, k, logits, topk_ids, topk_w, partial, splits, stream));
+                                      T, H, E, k, logits, topk_ids, topk_w, workspace, plan, stream));
 }
 
 size_t moe_dispatch_workspace_bytes(int T, int k, int E) {

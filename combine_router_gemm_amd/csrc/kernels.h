@@ -15,14 +15,21 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // ---- route ----
 struct RouteTiles {
   int BM, BN;
+  bool planes;  // the plane GEMM (router weight split once into three bf16 planes in the workspace)
 };
-RouteTiles route_tiles(int T, int xdt_bf16);
+RouteTiles route_tiles(int T, int H, int E, int xdt_bf16);
 bool route_fused(int T, int E);  // one fused kernel, no workspace
-int route_splits(int T, int H, int E, int xdt_bf16, int num_cus);
-int route_k_split(int H, int splits);
+// the launch plan: K splits, and the workspace: planes (planes_bytes, 256-aligned) then the fp32 partial
+// sums (partial_bytes, only with several splits)
+struct RoutePlan {
+  RouteTiles tiles;
+  int splits, k_split, nsplit;
+  size_t planes_bytes, partial_bytes;
+};
+RoutePlan route_plan(int T, int H, int E, int xdt_bf16, int num_cus);
 hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, const float* bias,
                         int64_t bias_stride, int T, int H, int E, int k, float* logits, int* ids, float* wts,
-                        float* partial, int splits, hipStream_t stream);
+                        void* workspace, const RoutePlan& plan, hipStream_t stream);
 
 // ---- dispatch ----
 constexpr int DISPATCH_TB = 256;  // tokens per counting block

@@ -8,11 +8,17 @@
 // Kernel 1 (route_gemm): split-K GEMM. Grid (token tiles, expert tiles, K splits); each workgroup
 //   writes an fp32 partial [T, E] for its K range. fp32 activations run on fp32 MFMA. bf16
 //   activations run on bf16 MFMA with the router weight split exactly into three bf16 parts, so
-//   every product is the exact fp32 product of the inputs and the sum is accumulated in fp32.
+//   every product is the exact fp32 product of the inputs and the sum is accumulated in fp32. With
+//   many tokens the weight is split once per call into three planes in the workspace
+//   (route_planes), which a direct-to-LDS GEMM then reads (route_gemm_planes); with few, each
+//   workgroup splits its weight tile on the way into LDS.
 // Kernel 2 (route_topk): sums the K-split partials in a fixed order (deterministic), adds the bias,
 //   (with a single split the partial buffer is the logits buffer itself, read then overwritten in place),
 //   writes the logits and selects the top-k per token with a lane-group arg-max: G lanes per token,
 //   each holding E/G logits, k rounds of a butterfly max over (value desc, expert id asc).
+#include <algorithm>
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "mfma.h"
@@ -626,40 +632,250 @@ __global__ __launch_bounds__(256) void route_small_kernel(const TX* __restrict__
   select_topk_wave<1>(val, taken, lane, t, true, k, 1, topk_ids, topk_w);
 }
 
+// ------------------------------------------------------------------------------------------------
+// Many tokens (bf16, T >= 2048, H % 64 == 0): the router weight split once per call into its three
+// exact bf16 planes, then a direct-to-LDS GEMM over the planes
+// ------------------------------------------------------------------------------------------------
+// planes [3][E][H] bf16: plane p of expert e at planes + (p * E + e) * H (split3_bf16 per element)
+__global__ __launch_bounds__(256) void route_planes_kernel(const float* __restrict__ w, int E, int H,
+                                                           uint16_t* __restrict__ planes) {
+  const int64_t n4 = (int64_t)E * H / 4;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+    float f[4];
+    unpack(ld16(w + i * 4), f);
+    uint16_t hv[4], mv[4], lv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split3_bf16(f[q], hv[q], mv[q], lv[q]);
+    const int64_t plane = (int64_t)E * H;
+    *reinterpret_cast<u32x2*>(planes + i * 4) = u32x2{hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16)};
+    *reinterpret_cast<u32x2*>(planes + plane + i * 4) =
+        u32x2{mv[0] | ((uint32_t)mv[1] << 16), mv[2] | ((uint32_t)mv[3] << 16)};
+    *reinterpret_cast<u32x2*>(planes + 2 * plane + i * 4) =
+        u32x2{lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16)};
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void route_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 256 tokens x 128 experts x 64-deep stages, 8 waves (4 x 2) of 64 x 64, two stage slots of 80 KB:
+// A = 256 x rows, B = the 3 planes x 128 experts (row p * 128 + e). Operands go global -> LDS with
+// buffer_load_dwordx4 ... lds (one wave instruction = 8 rows of 128 bytes), chunk c of LDS row r at
+// c ^ ((r >> 1) & 7), rows past T or E fetched at an out-of-range offset (zeros). Schedule: the barrier
+// that publishes stage s + 1 sits before the MFMAs of stage s's last K step; right after it the x loads
+// of stage s + 2 (the HBM stream) go into stage s's slot, one between MFMAs, and the plane loads of stage
+// s + 1 (L2-resident) go out between the MFMAs of stage s's first K step. Per K step a wave multiplies
+// its 2 x blocks by 2 expert blocks of each plane into the same accumulators. The grid is one
+// workgroup per (K split, token tile, expert tile), cut into eight contiguous ranges, one per XCD, so
+// the expert tiles of one token tile share an L2. Writes an fp32 partial [T, E] per K split.
+constexpr int RP_BM = 256, RP_BN = 128, RP_BK = 64, RP_WM = 4, RP_WN = 2, RP_NW = RP_WM * RP_WN;
+__global__ __launch_bounds__(RP_NW * 64) void route_gemm_planes_kernel(const bf16_t* __restrict__ x,
+                                                                      const uint16_t* __restrict__ planes, int T,
+                                                                      int H, int E, int k_split, int n_ttiles,
+                                                                      int n_etiles, int n_items,
+                                                                      float* __restrict__ partial) {
+  using Op = Op32;
+  constexpr int S = 32, ROWB = RP_BK * 2, CPR = 8, RPI = 8;
+  constexpr int A_ROWS = RP_BM, B_ROWS = 3 * RP_BN;
+  constexpr int A_INS = A_ROWS / RPI, B_INS = B_ROWS / RPI;
+  static_assert(A_INS % RP_NW == 0 && B_INS % RP_NW == 0, "even loads per wave");
+  constexpr int AW = A_INS / RP_NW, BW = B_INS / RP_NW, LPW = AW + BW;
+  constexpr int A_BYTES = A_ROWS * ROWB, STAGE = (A_ROWS + B_ROWS) * ROWB;
+  constexpr int TM = RP_BM / RP_WM / S, TN = RP_BN / RP_WN / S;
+  constexpr int KSTEPS = RP_BK / Op::KS;
+  static_assert(2 * STAGE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  // work item of this workgroup: (split, token tile, expert tile), expert tile fastest
+  int item = blockIdx.x;
+  if ((n_items & 7) == 0 && (int)gridDim.x == n_items) item = (blockIdx.x & 7) * (n_items >> 3) + (blockIdx.x >> 3);
+  const int et = item % n_etiles, tt = (item / n_etiles) % n_ttiles, split = item / (n_etiles * n_ttiles);
+  const int t0 = tt * RP_BM, e0 = et * RP_BN;
+  const int kbeg = split * k_split, kend = min(H, kbeg + k_split);
+  const int nk = (kend - kbeg) / RP_BK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / RP_WN, wn = wave % RP_WN;
+  const int OOB = 0x7ffffff0;
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)((int64_t)T * H * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t p_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)planes, (short)0, (int)((int64_t)3 * E * H * 2), 0x00020000);
+  auto swz = [](int r) { return (r >> 1) & 7; };
+
+  // this wave's loads: q < AW are x rows (instructions wave * AW + q), the rest plane rows
+  int voff[LPW];
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    const int r_in = lane / CPR, pos = lane % CPR;
+    if (q < AW) {
+      const int r = (wave * AW + q) * RPI + r_in;
+      voff[q] = t0 + r < T ? ((t0 + r) * H + kbeg) * 2 + ((pos ^ swz(r)) << 4) : OOB;
+    } else {
+      const int r = (wave * BW + q - AW) * RPI + r_in;  // B row: plane r / BN, expert e0 + r % BN
+      const int p = r / RP_BN, e = e0 + r % RP_BN;
+      voff[q] = e < E ? ((p * E + e) * H + kbeg) * 2 + ((pos ^ swz(r)) << 4) : OOB;
+    }
+  }
+  auto loff = [&](int q) { return q < AW ? (wave * AW + q) * 1024 : A_BYTES + (wave * BW + q - AW) * 1024; };
+  auto issue_one = [&](int st, int slot, int q) {
+    const int vo = voff[q] == OOB ? OOB : voff[q] + st * RP_BK * 2;
+    auto* dst = (__attribute__((address_space(3))) void*)(smem + slot * STAGE + loff(q));
+    if (q < AW) __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, dst, 16, vo, 0, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(p_rsrc, dst, 16, vo, 0, 0, 0);
+  };
+
+  typename Op::Acc acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < Op::NR; ++q) acc[i][j][q] = 0.f;
+
+  const int fr = lane & 31, fq = lane >> 5;
+  auto load_frags = [&](const unsigned char* base, int kk, u32x4 (&af)[TM][1], u32x4 (&bfg)[3][TN][1]) {
+    const int c = kk / 8 + fq;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wm * (RP_BM / RP_WM) + i * S + fr;
+      af[i][0] = ld16(base + r * ROWB + ((c ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = p * RP_BN + wn * (RP_BN / RP_WN) + j * S + fr;
+        bfg[p][j][0] = ld16(base + A_BYTES + r * ROWB + ((c ^ swz(r)) << 4));
+      }
+  };
+
+  if (nk > 0) {
+    // prologue: stage 0 into slot 0, the x loads of stage 1 into slot 1
+#pragma unroll
+    for (int q = 0; q < AW; ++q) issue_one(0, 0, q);
+#pragma unroll
+    for (int q = AW; q < LPW; ++q) issue_one(0, 0, q);
+    if (nk > 1) {
+#pragma unroll
+      for (int q = 0; q < AW; ++q) issue_one(1, 1, q);
+      route_wait_vmcnt<AW>();
+    } else {
+      route_wait_vmcnt<0>();
+    }
+    lds_barrier();
+    u32x4 af[2][TM][1], bfg[2][3][TN][1];
+    load_frags(smem, 0, af[0], bfg[0]);
+    auto stage = [&](int s, auto HAVE1, auto HAVE2) {
+      constexpr bool have1 = decltype(HAVE1)::value, have2 = decltype(HAVE2)::value;
+      const int slot = s & 1;
+      const unsigned char* base = smem + slot * STAGE;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        if (ks + 1 < KSTEPS) {
+          load_frags(base, (ks + 1) * Op::KS, af[(ks + 1) & 1], bfg[(ks + 1) & 1]);
+        } else if (have1) {
+          route_wait_vmcnt<0>();  // this wave's loads of stage s + 1
+          lds_barrier();          // stage s + 1 visible; no wave reads slot s & 1 any more
+          load_frags(smem + (slot ^ 1) * STAGE, 0, af[0], bfg[0]);
+        }
+        // the next K step's fragment reads stay ahead of this step's MFMAs (the scheduler would
+        // otherwise sink each read to just before its use and wait on it there)
+        __builtin_amdgcn_sched_barrier(0);
+        int m = 0;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int p = 0; p < 3; ++p) Op::step(acc[i][j], af[ks & 1][i], bfg[ks & 1][p][j]);
+            // one load between each group of three MFMAs: plane loads of stage s + 1 in the first K step,
+            // x loads of stage s + 2 in the last
+            if (ks == 0 && have1 && m < BW) issue_one(s + 1, slot ^ 1, AW + m);
+            if (ks == KSTEPS - 1 && have2 && m < AW) issue_one(s + 2, slot, m);
+            ++m;
+          }
+        if (ks == 0 && have1) {
+#pragma unroll
+          for (int q = TM * TN; q < BW; ++q) issue_one(s + 1, slot ^ 1, AW + q);
+        }
+        if (ks == KSTEPS - 1 && have2) {
+#pragma unroll
+          for (int q = TM * TN; q < AW; ++q) issue_one(s + 2, slot, q);
+        }
+      }
+    };
+    using Yes = std::integral_constant<bool, true>;
+    using No = std::integral_constant<bool, false>;
+    int s = 0;
+    for (; s + 2 < nk; ++s) stage(s, Yes{}, Yes{});
+    if (s + 1 < nk) stage(s++, Yes{}, No{});
+    stage(s, No{}, No{});
+  }
+
+  float* out = partial + (int64_t)split * T * E;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = e0 + wn * (RP_BN / RP_WN) + j * S + fr;
+#pragma unroll
+      for (int q = 0; q < Op::NR; ++q) {
+        const int row = t0 + wm * (RP_BM / RP_WM) + i * S + Op::out_row(lane, q);
+        if (row < T && col < E) out[(int64_t)row * E + col] = acc[i][j][q];
+      }
+    }
+}
+
 }  // namespace
 
-// Host-side planning. Tile shape: fp32 activations use 64x64 fp32-MFMA tiles; bf16 activations use
-// 128x128 bf16x3 tiles for many tokens and 64x64 for few. The split-K factor gives enough workgroups
-// to cover the chip twice, each split at least 256 K-elements long and a multiple of the 32-wide stage.
-RouteTiles route_tiles(int T, int xdt_bf16) {
-  if (xdt_bf16 && T >= 2048) return RouteTiles{128, 128};
-  return RouteTiles{64, 64};
+// Host-side planning. Tile shape: fp32 activations use 64x64 fp32-MFMA tiles; bf16 activations use the
+// plane GEMM (256 x 128 tiles, the weight split once into three bf16 planes) for many tokens when the
+// row length is a multiple of 64 and the operands fit 31-bit buffer offsets, 64x64 bf16x3 tiles for few.
+// The split-K factor gives enough workgroups to cover the chip (twice for the register-staged tiles,
+// once for the plane GEMM, whose 160 KB of LDS take a whole CU), each split at least 256 K-elements long
+// and a multiple of the stage depth.
+RouteTiles route_tiles(int T, int H, int E, int xdt_bf16) {
+  if (xdt_bf16 && T >= 2048 && H % RP_BK == 0 && (int64_t)T * H * 2 < 0x7ffffff0ll - 256 &&
+      (int64_t)3 * E * H * 2 < 0x7ffffff0ll - 256)
+    return RouteTiles{RP_BM, RP_BN, true};
+  return RouteTiles{64, 64, false};
 }
 
 bool route_fused(int T, int E) { return E <= 16 && T <= kRouteFusedMaxT; }
 
-int route_splits(int T, int H, int E, int xdt_bf16, int num_cus) {
-  if (route_fused(T, E)) return 1;
-  const RouteTiles rt = route_tiles(T, xdt_bf16);
-  const int tiles = ceil_div_host(T, rt.BM) * ceil_div_host(E, rt.BN);
-  int s = ceil_div_host(2 * num_cus, tiles > 0 ? tiles : 1);
+RoutePlan route_plan(int T, int H, int E, int xdt_bf16, int num_cus) {
+  RoutePlan p{};
+  p.tiles = route_tiles(T, H, E, xdt_bf16);
+  if (route_fused(T, E) || T <= 0) {
+    p.splits = p.nsplit = 1;
+    p.k_split = H;
+    return p;
+  }
+  const int tiles = ceil_div_host(T, p.tiles.BM) * ceil_div_host(E, p.tiles.BN);
+  int s = ceil_div_host((p.tiles.planes ? 1 : 2) * num_cus, tiles > 0 ? tiles : 1);
   // at least 256 K per split, and few enough splits that the partial sums stay a small share of the
   // traffic (the top-k kernel reads them all back)
   int smax = H / 256 > 0 ? H / 256 : 1;
   if (smax > kRouteMaxSplits) smax = kRouteMaxSplits;
   if (s > smax) s = smax;
   if (s < 1) s = 1;
-  return s;
-}
-
-int route_k_split(int H, int splits) {
-  int ks = ceil_div_host(H, splits);
-  return ceil_div_host(ks, RG_BK) * RG_BK;
+  const int align = p.tiles.planes ? RP_BK : RG_BK;
+  p.splits = s;
+  p.k_split = ceil_div_host(ceil_div_host(H, s), align) * align;
+  p.nsplit = ceil_div_host(H, p.k_split);
+  p.planes_bytes = p.tiles.planes ? align256((size_t)3 * E * H * 2) : 0;
+  p.partial_bytes = p.nsplit > 1 ? (size_t)p.nsplit * T * E * sizeof(float) : 0;
+  return p;
 }
 
 hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, const float* bias,
                         int64_t bias_stride, int T, int H, int E, int k, float* logits, int* ids, float* wts,
-                        float* partial, int splits, hipStream_t stream) {
+                        void* workspace, const RoutePlan& plan, hipStream_t stream) {
   if (route_fused(T, E)) {
     const unsigned blocks = (unsigned)T;
     const bool e8 = E <= 8;
@@ -676,14 +892,21 @@ hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, cons
 #undef MOE_ROUTE_SMALL
     return hipGetLastError();
   }
-  const int k_split = route_k_split(H, splits);
-  const int nsplit = ceil_div_host(H, k_split);
-  const RouteTiles rt = route_tiles(T, xdt_bf16);
+  const int k_split = plan.k_split;
+  const int nsplit = plan.nsplit;
+  const RouteTiles rt = plan.tiles;
+  // the partial sums: in the workspace past the planes with several K splits, else the logits themselves
+  float* partial = nsplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.planes_bytes) : logits;
   dim3 grid(ceil_div_host(T, rt.BM), ceil_div_host(E, rt.BN), nsplit);
-  if (xdt_bf16 && rt.BM == 128)
-    route_gemm_bf16x3_kernel<Op32, 128, 128, 2, 2><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H,
-                                                                       E, k_split, partial);
-  else if (xdt_bf16)
+  if (rt.planes) {
+    uint16_t* planes = static_cast<uint16_t*>(workspace);
+    const int64_t n4 = (int64_t)E * H / 4;
+    const unsigned pb = (unsigned)std::min<int64_t>(ceil_div_host64(n4, 256), 2048);
+    route_planes_kernel<<<pb, 256, 0, stream>>>(w_router, E, H, planes);
+    const int n_tt = ceil_div_host(T, RP_BM), n_et = ceil_div_host(E, RP_BN), n_items = n_tt * n_et * nsplit;
+    route_gemm_planes_kernel<<<n_items, RP_NW * 64, 0, stream>>>(static_cast<const bf16_t*>(x), planes, T, H, E, k_split,
+                                                                n_tt, n_et, n_items, partial);
+  } else if (xdt_bf16)
     route_gemm_bf16x3_kernel<Op32, 64, 64, 2, 2><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(x), w_router, T, H, E,
                                                                      k_split, partial);
   else

@@ -128,9 +128,10 @@ int moe_route(const void* x, moe_dtype_t xdt, const float* w_router, const float
               int64_t bias_row_stride, int T, int H, int E, int k, float* logits, int32_t* topk_ids,
               float* topk_w, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of scratch `workspace` moe_route needs for (T, H, E, xdt): fp32 partial sums when the H
- * reduction is split across workgroups (0 when it is not, e.g. for E <= 16 and T <= 4096; workspace
- * may then be NULL). */
+/* Bytes of scratch `workspace` moe_route needs for (T, H, E, xdt): for bf16 activations with
+ * T >= 2048 and H % 64 == 0, the router weight split into three exact bf16 planes (3 * E * H * 2
+ * bytes); fp32 partial sums when the H reduction is split across workgroups. 0 when neither applies
+ * (e.g. for E <= 16 and T <= 4096; workspace may then be NULL). */
 size_t moe_route_workspace_bytes(int T, int H, int E, moe_dtype_t xdt);
 
 /* Bytes of scratch `workspace` moe_dispatch needs for (T, k, E). */

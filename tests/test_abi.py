@@ -61,11 +61,13 @@ def test_workspace_sizes(lib):
     # h [rows_max, F] bf16 dominates the MLP workspace
     assert moe.moe_expert_mlp_workspace_bytes(4096, 8, 256, 8, 128, 2048, moe.MOE_BF16) >= 32768 * 2048 * 2
     assert moe.moe_expert_mlp_workspace_bytes(256, 2, 8, 1, 80, 256, moe.MOE_F32) >= 512 * 256 * 4
-    # the router needs scratch only when the H reduction is split: whole [T, E] fp32 partials
+    # the router's scratch: whole [T, E] fp32 partials when the H reduction is split, after (bf16, 2048+
+    # tokens, H % 64 == 0) the router weight's three bf16 planes, 256-byte aligned
     for T, H, E in ((16384, 7168, 256), (128, 4096, 8), (256, 128, 8), (4096, 7168, 256)):
         for xdt in (moe.MOE_BF16, moe.MOE_F32):
             n = moe.moe_route_workspace_bytes(T, H, E, xdt)
-            assert n % (T * E * 4) == 0 and n != T * E * 4
+            planes = ((3 * E * H * 2 + 255) // 256) * 256 if (xdt == moe.MOE_BF16 and T >= 2048) else 0
+            assert n >= planes and (n - planes) % (T * E * 4) == 0 and n - planes != T * E * 4
     # few experts and tokens: one fused kernel, no scratch; many experts: split-K partials
     assert moe.moe_route_workspace_bytes(128, 4096, 8, moe.MOE_BF16) == 0
     assert moe.moe_route_workspace_bytes(4096, 4096, 16, moe.MOE_F32) == 0

@@ -102,6 +102,8 @@ TOPK_ROWS_CASES = [
     (300, 128, 8, None, 128, 0), (1100, 192, 6, "vec", 2048, 0), (200, 320, 8, "rows", 4096, 0),
     (700, 384, 8, None, 7168, 0), (50, 448, 7, "vec", 448, 1), (129, 512, 8, "rows", 1024, 1),
     (1500, 256, 8, "rows", 256, 1), (3, 384, 8, None, 384, 0),
+    # 2048+ tokens with H % 64 == 0 take the plane GEMM: ragged token and expert tiles, one or several splits
+    (2500, 256, 8, "rows", 256, 0), (4100, 384, 8, None, 7168, 1), (2300, 448, 7, "vec", 1024, 0),
 ]
 
 
@@ -148,8 +150,8 @@ def _check_topk_ties(T, E, k, bias, H, off):
 
 # non-finite logits: a [T, E] bias of 0, NaN, +inf or -inf on one-hot router rows. A NaN logit ranks as -inf
 # and ties (also among infinities and NaN) go to the lower id, on every router kernel: fused small-E,
-# split-K with the lane-interleaved top-k, and split-K with the row-contiguous top-k
-NONFINITE_CASES = [(300, 8, 2), (257, 16, 8), (300, 40, 5), (129, 64, 8), (700, 256, 8), (50, 384, 8)]
+# split-K with the lane-interleaved top-k, split-K with the row-contiguous top-k, and the plane GEMM
+NONFINITE_CASES = [(300, 8, 2), (257, 16, 8), (300, 40, 5), (129, 64, 8), (700, 256, 8), (50, 384, 8), (2200, 256, 8)]
 
 
 @pytest.mark.parametrize("T,E,k", NONFINITE_CASES, ids=[f"T{c[0]}_E{c[1]}_k{c[2]}" for c in NONFINITE_CASES])
