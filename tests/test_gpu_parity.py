@@ -259,9 +259,13 @@ EDGE = [
     ("E512_k8", 300, 64, 512, 8, 32, 8, 5, "bf16", "zipf"),
     ("hot_overflow", 512, 128, 64, 6, 64, 1, 48, "bf16", "hot8"),
     ("many_rows_tile_edges", 700, 128, 4, 2, 160, 1, 300, "bf16", "uniform"),
-    # direct-to-LDS grouped GEMM: 128-row tiles (400 rows per expert), then 256-row tiles (2200 rows per
-    # local expert); F = 192 and H = 192 / 320 leave a ragged last column tile in both GEMMs
+    # loaded-to-LDS grouped GEMM: 320-row whole-expert tiles (400 rows per expert; 3-stage K loops, so no
+    # cross-tile prefetch), then 256-row ping-pong tiles (2200 rows per local expert); F = 192 and
+    # H = 192 / 320 leave a ragged last column tile in both GEMMs
     ("dl128_ragged", 900, 192, 4, 2, 192, 1, 400, "bf16", "zipf"),
+    # whole-expert tiles, two per workgroup (512 tiles per GEMM), even K-stage counts: the next tile's first
+    # stage is prefetched during the current one
+    ("xs_two_tiles_per_wg", 4096, 1024, 128, 8, 512, 1, 300, "bf16", "uniform"),
     # 128-row direct-to-LDS tiles (capacity 200 rows per expert), ragged
     ("dl128_cap200", 700, 128, 8, 2, 128, 2, 200, "bf16", "zipf"),
     ("dl256_ragged_R2", 2600, 320, 4, 2, 192, 2, 1100, "bf16", "zipf"),
