@@ -1404,18 +1404,21 @@ __global__ __launch_bounds__(512) void mlp_gemm_pp_kernel(GemmArgs args, int a_b
   constexpr int KPH = kPpKph, UPS = KSTEPS / KPH;  // K steps per phase, phases per stage and group
   static_assert(KSTEPS % KPH == 0, "phases split a stage evenly");
   constexpr int OUT_BYTES = BM * OUT_COLS * 2;
-  constexpr int SMEM = (2 * STAGE > OUT_BYTES + BM * 4 ? 2 * STAGE : OUT_BYTES + BM * 4);
+  constexpr int PLAN_OFF = (2 * STAGE > OUT_BYTES + BM * 4 ? 2 * STAGE : OUT_BYTES + BM * 4);
+  constexpr int PLAN_INTS = MOE_MAX_EXPERTS + 1;
+  constexpr int SMEM = PLAN_OFF + 2 * PLAN_INTS * 4;
   static_assert(TM >= 1 && TN >= 1, "wave tile too small");
   static_assert(SMEM <= 160 * 1024, "LDS");
-  // the two stage buffers; after the last stage the output tile and its destination rows reuse them
+  // the two stage buffers (after the last stage the output tile and its destination rows reuse them),
+  // then a copy of the plan's per-expert starts
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+  int* s_rs = reinterpret_cast<int*>(smem + PLAN_OFF);  // row start per local expert [0..El]
+  int* s_ts = s_rs + PLAN_INTS;                          // M-tile start per local expert [0..El]
 
   const bf16_t* A = static_cast<const bf16_t*>(args.A);
   const bf16_t* W = static_cast<const bf16_t*>(args.W);
   bf16_t* __restrict__ Out = static_cast<bf16_t*>(args.Out);
   const int El = args.El;
-  const int* row_start = args.plan + 2;
-  const int* tile_start = args.plan + 3 + El;
   const int n_tiles = (args.N + OUT_COLS - 1) / OUT_COLS;
   const int total = args.plan[0] * n_tiles;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1436,20 +1439,25 @@ __global__ __launch_bounds__(512) void mlp_gemm_pp_kernel(GemmArgs args, int a_b
     t_step = G >> 3;
   }
 
+  for (int i = tid; i <= El; i += NW * 64) {
+    s_rs[i] = args.plan[2 + i];
+    s_ts[i] = args.plan[3 + El + i];
+  }
+  lds_barrier();
+
   const int fr = lane & 31, fq = lane >> 5;
+  int l = 0;
   for (int tile = t_begin; tile < t_end; tile += t_step) {
-    int lo = 0, hi = El;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (tile_start[mid] * n_tiles <= tile) lo = mid;
-      else hi = mid;
-    }
-    const int l = lo;
-    const int mt_l = tile_start[l + 1] - tile_start[l];
-    const int local = tile - tile_start[l] * n_tiles;
+    // tiles list (local expert, N tile, M tile) in expert order and a workgroup's tiles increase: the
+    // expert is found by scanning on from the previous tile's (8 dependent scalar loads of a binary
+    // search over the plan in memory had cost about 2 us per tile)
+    while (__builtin_amdgcn_readfirstlane(s_ts[l + 1]) * n_tiles <= tile) ++l;
+    const int ts = __builtin_amdgcn_readfirstlane(s_ts[l]);
+    const int mt_l = __builtin_amdgcn_readfirstlane(s_ts[l + 1]) - ts;
+    const int local = tile - ts * n_tiles;
     const int nt = local / mt_l, mt = local % mt_l;
-    const int p0 = row_start[l] + mt * BM;
-    const int m_rows = min(BM, row_start[l + 1] - p0);
+    const int p0 = __builtin_amdgcn_readfirstlane(s_rs[l]) + mt * BM;
+    const int m_rows = min(BM, __builtin_amdgcn_readfirstlane(s_rs[l + 1]) - p0);
     const int n0 = nt * OUT_COLS;
     const __amdgpu_buffer_rsrc_t b_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)l * args.w_stride), (short)0, w_bytes, 0x00020000);
