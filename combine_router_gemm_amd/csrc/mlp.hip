@@ -1135,12 +1135,15 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_xs_kernel(GemmArgs args,
   };
   auto loff = [&](int q) { return q < AW ? (wave * AW + q) * 1024 : A_BYTES + (wave * BW + q - AW) * 1024; };
   __amdgpu_buffer_rsrc_t b_rsrc;
-  // this wave's load q (a compile-time index) of stage st into slot
+  // this wave's load q (a compile-time index) of stage st into slot. A whole expert's rows share each
+  // weight tile, so every weight byte is read once: the weight loads are non-temporal (cache policy bit
+  // 1), which leaves the L2 to the activation rows that the expert's N tiles share. On 256 experts of
+  // 192-512 rows at H 7168, F 2048: down 2530 -> 2347 us, gate/up 4362 -> 4324 us (same output bits)
   auto issue_one = [&](int st, int slot, int q) {
     const int vo = voff[q] == OOB ? OOB : voff[q] + st * BK * 2;
     auto* dst = (__attribute__((address_space(3))) void*)(smem + slot * STAGE + loff(q));
     if (q < AW) __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, dst, 16, vo, 0, 0, 0);
-    else __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dst, 16, vo, 0, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, dst, 16, vo, 0, 0, 2);
   };
 
   const int fr = lane & 31, fq = lane >> 5;
