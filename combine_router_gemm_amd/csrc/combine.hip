@@ -59,7 +59,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ out_
         for (int q = 0; q < VN; ++q) acc[q] = fmaf(s_w[j], val[q], acc[q]);
       }
     }
-    st16(y + (int64_t)t * H + (int64_t)v * VN, pack(acc));
+    // y is not read again in the layer: non-temporal stores (16384 tokens x 7168 from 67528 rows:
+    // 238 -> 234 us; 4096 x 7168 from 32768 rows: 89.5 -> 86.1 us)
+    st16_nt(y + (int64_t)t * H + (int64_t)v * VN, pack(acc));
   }
 }
 
