@@ -17,6 +17,7 @@
 //   writes the logits and selects the top-k per token with a lane-group arg-max: G lanes per token,
 //   each holding E/G logits, k rounds of a butterfly max over (value desc, expert id asc).
 #include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "common.h"
@@ -479,12 +480,102 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, i
 // with partial and logits aligned to it) instead of V single-float loads; the bias of the token is read
 // with its first split, and SPF further splits are in flight at a time. Same sums, in the same order, as
 // route_topk_kernel.
-template <int VW, int SPF>
+// Integer max over the 64 lanes of the wave, in every lane (same DPP pattern as wave_max; v_max_i32 needs
+// no NaN handling).
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_max_i32(int x) {
+  x = max(x, dpp_i32<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = max(x, dpp_i32<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = max(x, dpp_i32<0x141>(x));  // row_half_mirror
+  x = max(x, dpp_i32<0x140>(x));  // row_mirror
+  const int r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+  const int r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+// Order-preserving integer key of a float that is not NaN and not -0: a larger float has a larger key,
+// equal floats have equal keys, and key_float inverts it.
+__device__ __forceinline__ int float_key(float v) {
+  const int b = __float_as_int(v);
+  return b >= 0 ? b : b ^ 0x7fffffff;
+}
+__device__ __forceinline__ float key_float(int key) { return __int_as_float(key >= 0 ? key : key ^ 0x7fffffff); }
+
+// The same selection as select_topk_wave (the k largest values of the wave, ties to the lowest expert, expert
+// of lane g's i-th value g * V + i, then the softmax over the k selected values), for VT values per lane
+// known at compile time. val[i] for i >= V must be absent (passed as any value; they are never selected).
+// Each lane first sorts its values by key, descending and stable (equal values keep ascending i); every
+// round then takes the wave maximum of the lanes' current heads, and the lowest lane holding it (so the
+// lowest expert among equal values) moves its head on. No branches and no dynamic indexing.
+template <int VT>
+__device__ __forceinline__ void select_topk_sorted(const float (&val)[VT], int g, int t, int k, int V,
+                                                   int* __restrict__ topk_ids, float* __restrict__ topk_w) {
+  int key[VT], idx[VT];
+#pragma unroll
+  for (int i = 0; i < VT; ++i) {
+    key[i] = i < V ? float_key(val[i]) : INT_MIN;  // INT_MIN is below every value's key (-inf included)
+    idx[i] = i;
+  }
+#pragma unroll
+  for (int a = 1; a < VT; ++a)
+#pragma unroll
+    for (int b = a; b > 0; --b) {
+      const bool sw = key[b] > key[b - 1];  // strictly greater: equal keys keep their order
+      const int k0 = key[b - 1], k1 = key[b], i0 = idx[b - 1], i1 = idx[b];
+      key[b - 1] = sw ? k1 : k0;
+      key[b] = sw ? k0 : k1;
+      idx[b - 1] = sw ? i1 : i0;
+      idx[b] = sw ? i0 : i1;
+    }
+  int ptr = 0;  // this lane's next unselected position
+  float sel_v[MOE_MAX_TOPK];
+  int sel_e[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j < k) {
+      int head = INT_MIN, hidx = 0;
+#pragma unroll
+      for (int p = 0; p < VT; ++p) {
+        head = ptr == p ? key[p] : head;
+        hidx = ptr == p ? idx[p] : hidx;
+      }
+      const int m = wave_max_i32(head);
+      const uint64_t cand = __ballot(head == m);  // k <= E: m is a present value's key
+      const int wl = __builtin_ctzll(cand);
+      sel_e[j] = __builtin_amdgcn_readlane(g * V + hidx, wl);
+      sel_v[j] = key_float(m);
+      ptr += g == wl ? 1 : 0;
+    }
+  }
+  if (g < k) {
+    // softmax over the k selected logits (slot 0 holds the largest)
+    const float m = sel_v[0];
+    float sum = 0.f, mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        const float z = expf(sel_v[j] - m);
+        sum += z;
+        if (j == g) mine = z;
+      }
+    }
+    int myid = 0;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j == g) myid = sel_e[j];
+    topk_ids[(int64_t)t * k + g] = myid;
+    topk_w[(int64_t)t * k + g] = mine / sum;
+  }
+}
+
+template <int VW, int SPF, int VT>
 __global__ __launch_bounds__(256) void route_topk_rows_kernel(const float* partial, int splits,
                                                               const float* __restrict__ bias, int64_t bias_stride,
                                                               int T, int E, int k, float* logits,
                                                               int* __restrict__ topk_ids, float* __restrict__ topk_w) {
-  constexpr int VMAX = MOE_MAX_EXPERTS / 64;
+  constexpr int VMAX = VT;  // V = E / 64 logits per lane, rounded up to 1, 2, 4 or 8
   const int g = threadIdx.x & 63;
   const int t = (int)(((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6);
   const bool live = t < T;  // the same for the whole wave
@@ -564,7 +655,7 @@ __global__ __launch_bounds__(256) void route_topk_rows_kernel(const float* parti
     }
   }
   // live is uniform across the wave (one token per wave)
-  if (live) select_topk_wave<VMAX>(val, taken, g, t, true, k, V, topk_ids, topk_w);
+  if (live) select_topk_sorted<VMAX>(val, g, t, k, V, topk_ids, topk_w);
 }
 
 // Few experts: one workgroup of 256 threads per token computes the logits directly. Thread i
@@ -918,19 +1009,25 @@ hipError_t launch_route(const void* x, int xdt_bf16, const float* w_router, cons
     const int blocks = ceil_div_host(T, 4);  // four tokens (waves) per workgroup
     // with few tokens every split is loaded at once (latency); with many, four at a time (occupancy)
     const bool wide = T <= kRouteTopkWideMaxT;
-#define MOE_ROUTE_ROWS(VW)                                                                                       \
-  do {                                                                                                         \
-    if (wide)                                                                                                  \
-      route_topk_rows_kernel<VW, kRouteMaxSplits><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, \
-                                                                               T, E, k, logits, ids, wts);      \
-    else                                                                                                       \
-      route_topk_rows_kernel<VW, 4><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k,    \
-                                                                logits, ids, wts);                              \
-  } while (0)
-    if (V % 4 == 0 && al % 16 == 0) MOE_ROUTE_ROWS(4);
-    else if (V % 2 == 0 && al % 8 == 0) MOE_ROUTE_ROWS(2);
-    else MOE_ROUTE_ROWS(1);
-#undef MOE_ROUTE_ROWS
+    // VT: logits per lane rounded up to 1, 2, 4 or 8 (E <= 512); VW: the vector width of the row loads
+    auto rows = [&](auto VW_C, auto VT_C) {
+      constexpr int VW = decltype(VW_C)::value, VT = decltype(VT_C)::value;
+      if (wide)
+        route_topk_rows_kernel<VW, kRouteMaxSplits, VT><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride,
+                                                                                    T, E, k, logits, ids, wts);
+      else
+        route_topk_rows_kernel<VW, 4, VT><<<blocks, 256, 0, stream>>>(partial, nsplit, bias, bias_stride, T, E, k,
+                                                                      logits, ids, wts);
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    using I8 = std::integral_constant<int, 8>;
+    const int vw = V % 4 == 0 && al % 16 == 0 ? 4 : (V % 2 == 0 && al % 8 == 0 ? 2 : 1);
+    if (V == 1) rows(I1{}, I1{});
+    else if (V == 2) (vw >= 2 ? rows(I2{}, I2{}) : rows(I1{}, I2{}));
+    else if (V <= 4) (vw == 4 ? rows(I4{}, I4{}) : vw == 2 ? rows(I2{}, I4{}) : rows(I1{}, I4{}));
+    else (vw == 4 ? rows(I4{}, I8{}) : vw == 2 ? rows(I2{}, I8{}) : rows(I1{}, I8{}));
     return hipGetLastError();
   }
   // lane-group size: smallest power of two >= E, between 8 and 64
