@@ -55,6 +55,9 @@ namespace {
 // plan layout (int32): [0] total M-tiles, [1] total rows, [2 .. 2+El] row start per local expert
 // (El+1 entries), [3+El .. 3+2El] M-tile start per local expert (El+1 entries).
 constexpr int PLAN_THREADS = 1024;  // >= MOE_MAX_EXPERTS: one thread per (local or global) expert
+// after the plan: counters of the K-split tail tiles of the whole-expert gate/up GEMM (zeroed by the plan
+// kernel before every GEMM)
+constexpr int kSplitSlots = 512;
 constexpr int PLAN_ROWS_PER_WG = 4096;
 
 __global__ __launch_bounds__(PLAN_THREADS) void mlp_plan_kernel(const int* __restrict__ kept,
@@ -119,6 +122,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void mlp_plan_kernel(const int* __res
     row_start[tid] = s_rows[tid];
     tile_start[tid] = s_tiles[tid];
   }
+  if (blockIdx.x == 0)
+    for (int i = tid; i < kSplitSlots; i += PLAN_THREADS) plan[4 + 2 * El + i] = 0;
   // global expert e = r*El + l lands after the rows of experts l, El + l, ..., (r-1)*El + l
   if (tid < E) {
     const int l = tid % El, r = tid / El;
@@ -178,6 +183,7 @@ struct GemmArgs {
   void* y;               // [T, N] combine output
   int k;
   int out_bytes;         // bytes of Out when 31-bit buffer offsets cover it, else 0
+  int* split_ctr;        // gate/up: kSplitSlots zeroed counters for the K-split tail tiles, or nullptr
 };
 
 // Eight OCP E4M3 codes (q.x, q.y, little-endian bytes) times their block scale sc (a power of two) as
@@ -1069,22 +1075,47 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_xs_kernel(GemmArgs args,
   }
   lds_barrier();
 
+  // Work units. The tile list is cut into eight equal contiguous ranges, one per XCD (when the grid is a
+  // multiple of 8: workgroup b runs on XCD b % 8); the gx workgroups of XCD x take its n_x tiles in rounds,
+  // workgroup j the tiles j, j + gx, ... When the last round is at most half full (0 < tail <= gx / 2; gate/up
+  // GEMM, stage count a multiple of 4, room for the partials), each tail tile is cut into two K halves and
+  // workgroup j of the last round takes half j & 1 of tail tile j >> 1, so no workgroup idles through it.
+  // Both halves store their fp32 accumulators and count their arrival; the second to arrive adds the other
+  // half's and finishes the tile (the sum of the two halves is the same whichever arrives first).
   const int G = gridDim.x;
-  int t_begin = blockIdx.x, t_end = total, t_step = G;
+  int xcd = 0, wj = blockIdx.x, gx = G, base = 0, n_x = total;
   if ((G & 7) == 0 && G >= 8) {
-    const int x = blockIdx.x & 7, per = (total + 7) >> 3;
-    t_begin = x * per + (blockIdx.x >> 3);
-    t_end = min(total, (x + 1) * per);
-    t_step = G >> 3;
+    const int per = (total + 7) >> 3;
+    xcd = blockIdx.x & 7;
+    wj = blockIdx.x >> 3;
+    gx = G >> 3;
+    base = xcd * per;
+    n_x = max(0, min(total, base + per) - base);
   }
-  if (t_begin >= t_end) return;
+  const int rounds = n_x / gx, tail = n_x - rounds * gx;
+  constexpr int PART_BYTES = NW * 64 * TM * NACC * Op::NR * 4;  // one half's fp32 accumulators
+  int part_off = 0;
+  bool split = false;
+  if (GATED && args.split_ctr != nullptr && (nk & 3) == 0 && tail > 0 && 2 * tail <= gx && (G >> 1) <= kSplitSlots &&
+      args.out_bytes > 0) {
+    // the partials live in Out's rows past the GEMM's rows (h rows that no later step reads)
+    const int64_t off = ((int64_t)args.plan[1] * args.ldo * 2 + 255) & ~(int64_t)255;
+    split = off + (int64_t)(G >> 1) * 2 * PART_BYTES <= (int64_t)args.out_bytes;
+    part_off = (int)off;
+  }
+  const int n_full = rounds + (!split && wj < tail ? 1 : 0);
+  const int n_units = n_full + (split && wj < 2 * tail ? 1 : 0);
+  if (n_units == 0) return;
 
-  // a tile's expert, N tile and rows. Tiles list (local expert, N tile, M tile) in expert order and a
-  // workgroup's tiles increase, so the expert is found by scanning on from the previous tile's.
+  // a unit's expert, N tile, rows and K range. Tiles list (local expert, N tile, M tile) in expert order and
+  // a workgroup's tiles increase, so the expert is found by scanning on from the previous tile's.
   struct TileP {
     int l, nt, p0, m_rows, n0;
+    int k0, nks, half, slot;  // first stage, stages, K half (-1: the whole K) and its counter
   };
-  auto tile_params = [&](int tile, int l) {
+  auto tile_params = [&](int u, int l) {
+    const bool hu = GATED && u >= n_full;  // only the gate/up GEMM splits
+    const int tile = hu ? base + rounds * gx + (wj >> 1) : base + wj + u * gx;
     while (__builtin_amdgcn_readfirstlane(s_ts[l + 1]) * n_tiles <= tile) ++l;
     const int ts = __builtin_amdgcn_readfirstlane(s_ts[l]), mt_l = __builtin_amdgcn_readfirstlane(s_ts[l + 1]) - ts;
     const int local = tile - ts * n_tiles;
@@ -1095,6 +1126,10 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_xs_kernel(GemmArgs args,
     t.p0 = __builtin_amdgcn_readfirstlane(s_rs[l]) + mt * BM;
     t.m_rows = min(BM, __builtin_amdgcn_readfirstlane(s_rs[l + 1]) - t.p0);
     t.n0 = nt * OUT_COLS;
+    t.half = hu ? (wj & 1) : -1;
+    t.nks = hu ? nk >> 1 : nk;
+    t.k0 = hu ? t.half * t.nks : 0;
+    t.slot = xcd * (gx >> 1) + (wj >> 1);
     return t;
   };
   // this wave's loads: q < AW are A instructions wave * AW + q, q >= AW are B instructions wave * BW + q - AW;
@@ -1106,7 +1141,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_xs_kernel(GemmArgs args,
     for (int q = 0; q < AW; ++q) {
       const int r = (wave * AW + q) * RPI + lane / CPR;
       const int chunk = (lane % CPR) ^ dl_swz<1, CPR>(r);
-      voff[q] = r < t.m_rows ? src[q] * args.lda * 2 + chunk * 16 : OOB;
+      voff[q] = r < t.m_rows ? src[q] * args.lda * 2 + chunk * 16 + t.k0 * BK * 2 : OOB;
     }
   };
   auto lookup_a = [&](const TileP& t, int (&src)[AW]) {
@@ -1127,7 +1162,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_xs_kernel(GemmArgs args,
         ncol = t.n0 + r;
         wrow = ncol;
       }
-      voff[q] = ncol < args.N ? wrow * args.K * 2 + chunk * 16 : OOB;
+      voff[q] = ncol < args.N ? wrow * args.K * 2 + chunk * 16 + t.k0 * BK * 2 : OOB;
     }
   };
   auto b_rsrc_of = [&](const TileP& t) {
@@ -1174,7 +1209,7 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_xs_kernel(GemmArgs args,
   // wait on LDS, or those waits fall back to waiting for everything).
   auto run = [&](auto PF_C) {
   constexpr bool PF = decltype(PF_C)::value;
-  TileP cur = tile_params(t_begin, 0);
+  TileP cur = tile_params(0, 0);
   {
     int src[AW];
     lookup_a(cur, src);
@@ -1189,9 +1224,10 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_xs_kernel(GemmArgs args,
 #pragma unroll
     for (int q = 0; q < AW; ++q) issue_one(0, 0, q);
   }
-  for (int tile = t_begin; tile < t_end; tile += t_step) {
-    const int next = tile + t_step;
-    const bool has_next = next < t_end;
+  for (int u = 0; u < n_units; ++u) {
+    const int next = u + 1;
+    const bool has_next = next < n_units;
+    const int nk = GATED ? cur.nks : args.K / BK;  // this unit's stages
     const bool pf = PF && has_next;
     typename Op::Acc acc[TM][NACC];
 #pragma unroll
@@ -1297,6 +1333,45 @@ __global__ __launch_bounds__(WM* WN * 64) void mlp_gemm_xs_kernel(GemmArgs args,
     for (; s + 2 < nk; ++s) stage(s, Yes{}, Yes{}, P0{});
     if (s + 1 < nk) stage(s++, Yes{}, No{}, P1{});
     stage(s, No{}, No{}, P2{});
+
+    // a K half: store this half's fp32 accumulators (agent scope, written through to the level coherent
+    // across the XCDs), wait for them, then count the arrival. The first half to arrive is done; the second
+    // adds the first's accumulators (loaded only after its count returned) and finishes the tile. The
+    // ordering argument is the fused combine's (tile_arrive_combine).
+    if (GATED && cur.half >= 0) {
+      const __amdgpu_buffer_rsrc_t p_rsrc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)Out, (short)0, args.out_bytes, 0x00020000);
+      const int own = part_off + (cur.slot * 2 + cur.half) * PART_BYTES + tid * 16;
+      const int oth = part_off + (cur.slot * 2 + (cur.half ^ 1)) * PART_BYTES + tid * 16;
+      constexpr int SEGS = Op::NR / 4;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NACC; ++jj)
+#pragma unroll
+          for (int q4 = 0; q4 < SEGS; ++q4) {
+            const int seg = (i * NACC + jj) * SEGS + q4;
+            const u32x4 v = {__float_as_uint(acc[i][jj][4 * q4]), __float_as_uint(acc[i][jj][4 * q4 + 1]),
+                             __float_as_uint(acc[i][jj][4 * q4 + 2]), __float_as_uint(acc[i][jj][4 * q4 + 3])};
+            st16_agent(p_rsrc, own + seg * (NW * 64 * 16), v);
+          }
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (tid == 0) s_orow[0] = atomicAdd(&args.split_ctr[cur.slot], 1);
+      lds_barrier();
+      if (__builtin_amdgcn_readfirstlane(s_orow[0]) == 0) break;  // a half unit is a workgroup's last unit
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NACC; ++jj)
+#pragma unroll
+          for (int q4 = 0; q4 < SEGS; ++q4) {
+            const int seg = (i * NACC + jj) * SEGS + q4;
+            const u32x4 v = ld16_agent(p_rsrc, oth + seg * (NW * 64 * 16));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][jj][4 * q4 + e] += __uint_as_float(v[e]);
+          }
+    }
 
     // epilogue: the waves write their bf16 results to the staging area (lane l holds column l % 32,
     // rows 8*(q/4) + 4*(l/32) + q%4 of each 32x32 block), then every lane stores whole 16-byte row chunks.
@@ -1726,7 +1801,7 @@ int persistent_grid(int64_t max_tiles, int num_cus, int wpc) {
 
 }  // namespace
 
-size_t mlp_plan_ints(int El) { return 2 + 2 * (size_t)(El + 1); }
+size_t mlp_plan_ints(int El) { return 2 + 2 * (size_t)(El + 1) + kSplitSlots; }
 
 namespace {
 // the direct-to-LDS kernel addresses its operands with 31-bit buffer offsets and stages 64-deep K slices
@@ -1906,6 +1981,9 @@ hipError_t launch_expert_mlp(const void* send_buf, int xdt_bf16, const moe_layou
   gu.a_bytes = buffer_bytes(rows_max * H * (xdt_bf16 ? 2 : 4));
   gu.w_bytes = buffer_bytes(gu.w_stride * (xdt_bf16 ? 2 : 4));
   gu.k_rotate = k_rotate_for(H, xdt_bf16 ? 2 : 4);
+  // the whole-expert kernel keeps the fp32 partials of its K-split tail tiles in h's rows past the total
+  gu.out_bytes = buffer_bytes(rows_max * F * (xdt_bf16 ? 2 : 4));
+  gu.split_ctr = own_plan ? plan + 4 + 2 * El : nullptr;
 
   GemmArgs dn{};
   dn.A = hbuf;
