@@ -53,10 +53,9 @@ namespace {
 // plan
 // ------------------------------------------------------------------------------------------------
 // plan layout (int32): [0] total M-tiles, [1] total rows, [2 .. 2+El] row start per local expert
-// (El+1 entries), [3+El .. 3+2El] M-tile start per local expert (El+1 entries).
+// (El+1 entries), [3+El .. 3+2El] M-tile start per local expert (El+1 entries), then kSplitSlots counters
+// of the K-split tail tiles of the whole-expert gate/up GEMM, zeroed by the plan kernel before every GEMM.
 constexpr int PLAN_THREADS = 1024;  // >= MOE_MAX_EXPERTS: one thread per (local or global) expert
-// after the plan: counters of the K-split tail tiles of the whole-expert gate/up GEMM (zeroed by the plan
-// kernel before every GEMM)
 constexpr int kSplitSlots = 512;
 constexpr int PLAN_ROWS_PER_WG = 4096;
 

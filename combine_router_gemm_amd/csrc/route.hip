@@ -15,7 +15,9 @@
 // Kernel 2 (route_topk): sums the K-split partials in a fixed order (deterministic), adds the bias,
 //   (with a single split the partial buffer is the logits buffer itself, read then overwritten in place),
 //   writes the logits and selects the top-k per token with a lane-group arg-max: G lanes per token,
-//   each holding E/G logits, k rounds of a butterfly max over (value desc, expert id asc).
+//   each holding E/G logits, k rounds of a butterfly max over (value desc, expert id asc). When E is a
+//   multiple of 64 (route_topk_rows), a wave per token: each lane sorts its E/64 logits once and the k
+//   rounds take the wave maximum of the lanes' current heads (same selection).
 #include <algorithm>
 #include <climits>
 #include <type_traits>
@@ -475,11 +477,6 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* partial, i
   select_topk<G, VMAX>(val, taken, g, t, live, k, topk_ids, topk_w);
 }
 
-// E = 64 V (V <= 8): one wave per token, lane g holding the V consecutive experts g V .. g V + V - 1, so
-// the lane reads its part of each split's row with V / VW loads of VW floats (VW = 4, 2 or 1, dividing V,
-// with partial and logits aligned to it) instead of V single-float loads; the bias of the token is read
-// with its first split, and SPF further splits are in flight at a time. Same sums, in the same order, as
-// route_topk_kernel.
 // Integer max over the 64 lanes of the wave, in every lane (same DPP pattern as wave_max; v_max_i32 needs
 // no NaN handling).
 template <int CTRL>
@@ -570,6 +567,11 @@ __device__ __forceinline__ void select_topk_sorted(const float (&val)[VT], int g
   }
 }
 
+// E = 64 V (V <= 8): one wave per token, lane g holding the V consecutive experts g V .. g V + V - 1, so
+// the lane reads its part of each split's row with V / VW loads of VW floats (VW = 4, 2 or 1, dividing V,
+// with partial and logits aligned to it) instead of V single-float loads; the bias of the token is read
+// with its first split, and SPF further splits are in flight at a time. Same sums, in the same order, as
+// route_topk_kernel. VT is V rounded up to 1, 2, 4 or 8; the selection is select_topk_sorted.
 template <int VW, int SPF, int VT>
 __global__ __launch_bounds__(256) void route_topk_rows_kernel(const float* partial, int splits,
                                                               const float* __restrict__ bias, int64_t bias_stride,
