@@ -273,6 +273,11 @@ EDGE = [
     ("dec64_multi_mtile", 300, 128, 8, 2, 96, 1, 100, "bf16", "zipf"),
     # one counting block (T <= 256) scans all 512 experts itself
     ("E512_one_block", 200, 64, 512, 8, 32, 8, 4, "bf16", "zipf"),
+    # whole-expert gate/up GEMM with a K-split last round: about 288 M tiles x 10 N tiles (F 1280) leave 1-16 tail
+    # tiles per XCD range of 256 workgroups, each cut into two K halves (4 stages -> 2 + 2) that meet through the
+    # split counters; the hot-8 routing drops about 61K pairs, so h has rows free past the kept rows for the fp32
+    # partials (64 split tiles with this seed)
+    ("xs_split_tail_hot8", 16384, 256, 256, 8, 1280, 1, 512, "bf16", "hot8"),
 ]
 
 
