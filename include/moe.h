@@ -191,7 +191,9 @@ size_t moe_expert_mlp_workspace_bytes(int T, int k, int E, int R, int C, int F, 
  *   w_gate_up  [El, 2F, H] (xdt): rows 0..F-1 are Wg, rows F..2F-1 are Wu (nn.Linear [out, in])
  *   w_down     [El, H, F] (xdt)
  *   out_buf    [rows_max, H] (xdt) output, row-aligned with send_buf; rows >= total unspecified
- *   workspace  device scratch of at least moe_expert_mlp_workspace_bytes(...) bytes
+ *   workspace  device scratch of at least moe_expert_mlp_workspace_bytes(...) bytes: the tile plan and
+ *              its counters, the gather map and h; no contents need clearing between calls, and calls
+ *              that overlap must use separate workspaces
  * Requires H % 8 == 0 and F % 8 == 0. bf16 runs on bf16 MFMA, fp32 on fp32 MFMA.
  */
 int moe_expert_mlp(const void* send_buf, moe_dtype_t xdt, const moe_layout_t* layout,
